@@ -1,0 +1,229 @@
+"""CPU oracle for the KV-compose plan build, current-row scatter and slot-dense
+page gather.
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg are the only users.  Nothing in gather_plan_build_amd/ may
+import this package, and this package imports nothing from there.
+
+Two independent routes to the same bytes:
+
+* ``plan`` / ``compose_layer`` run the method's steps in order (C, plain
+  loops, gpb_oracle.c): validate, counts, spans, page inverse, staging page
+  inverse, gather descriptors, ragged descriptors, staging rows, then per
+  layer zero staging, scatter rows, gather pages.
+* ``closed_form.dense`` writes the composed dense buffer straight from its
+  definition per request (prefix pool rows, current rows, zero tail).
+
+Citations are to the commit pages of the sglang fork (page id = commit hash
+in the page address):
+  page d63fbd4, commit "current rows written straight into staging" -- the
+    staging-direct exchange, index_copy_ fill, [pool || staging] table;
+  page d63fbd4, commit "compose_v2" -- -1 descriptors zero-fill;
+  page d63fbd4, commit "cut per-layer CPU on the prefill launch path" -- the
+    ragged int32 descriptor names and per-batch slot spans;
+  page 0d87bc5, commit "prefetch staging exchange" -- page 0 dummy, staging
+    slot = batch current index + 1.
+
+Parity status per function (pins in tests/test_oracle_pins.py):
+  validate, counts, plan (spans, slot_pages, page_inverse,
+  staging_page_inverse, owner, src, writer, staging_rows, mixed_locs),
+  compose_layer, closed_form.dense -- pinned (brute force on tagged rows,
+  closed form, library special cases, hand-derived worked example);
+  q_lens, kv_lens, q_starts, k_bases, current_bases, q_bases -- the pages
+  give only their names; pinned to the stated definitions through the dense
+  and staging geometry they must agree with; "parity unpinned" as far as
+  the pages themselves go.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+from . import closed_form  # noqa: F401  (re-exported)
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+# validation result codes (gpb_oracle.c)
+OK, BAD_SHAPE, BAD_PAGE, CAPACITY, TOO_LARGE = 0, 1, 2, 3, 4
+
+PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
+               "q_starts", "k_bases", "q_bases", "current_bases", "slot_pages",
+               "owner", "src", "page_inverse", "staging_page_inverse", "writer",
+               "staging_rows", "mixed_locs")
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
+    return a, a.ctypes.data_as(_I32P)
+
+
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data if a.size else 0)
+
+
+class Oracle:
+    """The C oracle loaded from one shared library (the default build, or a
+    variant built elsewhere, e.g. a planted mistake in a test)."""
+
+    def __init__(self, lib_path):
+        lib = ctypes.CDLL(lib_path)
+        lib.gpbo_validate.restype = ctypes.c_int
+        lib.gpbo_plan.restype = ctypes.c_int
+        lib.gpbo_layer.restype = ctypes.c_int
+        lib.gpbo_counts.restype = None
+        self.lib = lib
+        self.path = lib_path
+
+    def validate(self, bs, page_size, row_bytes, n_pool_pages, n_pool_entries,
+                 n_writers, staging_cap_pages, prefix_pages, cur_tokens,
+                 req_pages):
+        """O1: 0 if the batch is well formed, else a positive reason code."""
+        P, pP = _i32(prefix_pages)
+        c, pc = _i32(cur_tokens)
+        g, pg = _i32(req_pages)
+        if bs < 0 or len(P) < bs or len(c) < bs or page_size < 1:
+            return BAD_SHAPE
+        if (P[:bs] < 0).any() or (c[:bs] < 0).any():
+            return BAD_SHAPE
+        # gpb_oracle.c reads as many page ids as the batch has pages
+        n_pages = int(P[:bs].astype(np.int64).sum()
+                      + ((c[:bs].astype(np.int64) + page_size - 1) // page_size).sum())
+        if n_pages != len(g):
+            return BAD_SHAPE
+        return self.lib.gpbo_validate(bs, page_size, row_bytes, n_pool_pages,
+                                      n_pool_entries, n_writers,
+                                      staging_cap_pages, pP, pc, pg)
+
+    def counts(self, bs, page_size, prefix_pages, cur_tokens):
+        """O2: (S, T, NCP) = dense slots, current rows, current pages."""
+        P, pP = _i32(prefix_pages)
+        c, pc = _i32(cur_tokens)
+        out = (ctypes.c_int64 * 3)()
+        self.lib.gpbo_counts(bs, page_size, pP, pc, out)
+        return int(out[0]), int(out[1]), int(out[2])
+
+    def plan(self, bs, page_size, row_bytes, n_pool_pages, n_pool_entries,
+             n_writers, staging_cap_pages, prefix_pages, cur_tokens, req_pages):
+        """O3..O9: the per-batch plan as a dict of int32 numpy arrays.
+
+        Raises ValueError(code) when validation fails (fail fast)."""
+        rc = self.validate(bs, page_size, row_bytes, n_pool_pages,
+                           n_pool_entries, n_writers, staging_cap_pages,
+                           prefix_pages, cur_tokens, req_pages)
+        if rc != OK:
+            raise ValueError(rc)
+        S, T, NCP = self.counts(bs, page_size, prefix_pages, cur_tokens)
+        sizes = {"slot_base": bs, "prefix_span": 2 * bs, "current_span": 2 * bs,
+                 "q_lens": bs, "kv_lens": bs, "q_starts": bs, "k_bases": bs,
+                 "q_bases": bs, "current_bases": bs, "slot_pages": S,
+                 "owner": S, "src": S, "page_inverse": n_pool_pages,
+                 "staging_page_inverse": n_pool_pages, "writer": NCP,
+                 "staging_rows": T, "mixed_locs": T}
+        # -7 marks entries the oracle never wrote; each array carries a guard
+        # tail as long as itself that must stay untouched
+        out = {k: np.full(2 * sizes[k] + 64, -7, dtype=np.int32) for k in PLAN_FIELDS}
+        P, pP = _i32(prefix_pages)
+        c, pc = _i32(cur_tokens)
+        g, pg = _i32(req_pages)
+        rc = self.lib.gpbo_plan(bs, page_size, row_bytes, n_pool_pages,
+                                n_pool_entries, n_writers, staging_cap_pages,
+                                pP, pc, pg,
+                                *[out[k].ctypes.data_as(_I32P) for k in PLAN_FIELDS])
+        if rc != OK:
+            raise ValueError(rc)
+        for k in PLAN_FIELDS:
+            assert np.all(out[k][sizes[k]:] == -7), "oracle wrote past " + k
+        return {k: out[k][:sizes[k]].copy() for k in PLAN_FIELDS}
+
+    def compose_layer(self, table, cur, staging_rows, owner, src, page_size,
+                      row_bytes, staging):
+        """O10: one layer.
+
+        ``table``: list of uint8 numpy arrays, one arena per pointer-table
+        entry (the staging slabs are views into ``staging``).  ``staging``
+        (uint8, whole rows) is zeroed, receives the scattered current rows,
+        then the gather reads the table.  Returns (dense uint8
+        [n_slots*page_size, row_bytes], bad) where bad flags an out-of-range
+        descriptor or staging row."""
+        RB = int(row_bytes)
+        n_slots = int(len(owner))
+        assert staging.dtype == np.uint8 and staging.flags.c_contiguous
+        assert staging.size % RB == 0
+        cur = np.ascontiguousarray(cur, dtype=np.uint8)
+        n_rows = int(len(staging_rows))
+        assert cur.size >= n_rows * RB
+        dense = np.empty((n_slots * page_size, RB), dtype=np.uint8)
+        n_tab = max(len(table), 1)
+        ptrs = (ctypes.c_void_p * n_tab)(*[t.ctypes.data for t in table])
+        pages = (ctypes.c_int64 * n_tab)(*[t.size // (page_size * RB) for t in table])
+        sr, psr = _i32(staging_rows)
+        ow, pow_ = _i32(owner)
+        sc, psc = _i32(src)
+        bad = self.lib.gpbo_layer(ptrs, pages, len(table), _p(staging),
+                                  ctypes.c_int64(staging.size // RB), _p(cur),
+                                  n_rows, psr, pow_, psc, n_slots, page_size,
+                                  RB, _p(dense))
+        return dense, bool(bad)
+
+
+def pointer_table(pool, staging, n_pool_entries, n_writers, staging_cap_pages,
+                  page_size, row_bytes):
+    """The [pool entries || staging slabs] table as a list of arrays: NP
+    aliases of the one pool arena (every pool entry is this GPU's pool), then
+    W slabs carved one after another from ``staging``, CAP pages each."""
+    slab = staging_cap_pages * page_size * row_bytes
+    flat = staging.reshape(-1)
+    return [pool.reshape(-1)] * n_pool_entries + \
+        [flat[w * slab:(w + 1) * slab] for w in range(n_writers)]
+
+
+_default = None
+
+
+def default():
+    """The oracle built from gpb_oracle.c in this directory."""
+    global _default
+    if _default is None:
+        _default = Oracle(_build.build(force=False))
+    return _default
+
+
+def validate(*a, **k):
+    return default().validate(*a, **k)
+
+
+def counts(*a, **k):
+    return default().counts(*a, **k)
+
+
+def plan(*a, **k):
+    return default().plan(*a, **k)
+
+
+def compose_layer(*a, **k):
+    return default().compose_layer(*a, **k)
+
+
+def plan_for(batch, orc=None):
+    """plan() for a workloads.Batch."""
+    o = orc or default()
+    return o.plan(batch.bs, batch.page_size, batch.row_bytes, batch.n_pool_pages,
+                  batch.n_pool_entries, batch.n_writers, batch.staging_cap_pages,
+                  batch.prefix_pages, batch.cur_tokens, batch.req_pages)
+
+
+def layer_for(batch, plan_arrays, pool, cur, staging, orc=None):
+    """compose_layer() for a workloads.Batch with its pool arena, current
+    rows and staging region (numpy uint8)."""
+    o = orc or default()
+    table = pointer_table(pool, staging, batch.n_pool_entries, batch.n_writers,
+                          batch.staging_cap_pages, batch.page_size,
+                          batch.row_bytes)
+    return o.compose_layer(table, cur, plan_arrays["staging_rows"],
+                           plan_arrays["owner"], plan_arrays["src"],
+                           batch.page_size, batch.row_bytes, staging)
+
+
+def lib_dir():
+    return os.path.dirname(os.path.abspath(__file__))

@@ -1,0 +1,103 @@
+"""Planted mistakes in the oracle must fail a pin.
+
+Each case rewrites one line of oracle/gpb_oracle.c (a dropped term, a wrong
+index or bound, an inclusive instead of exclusive sum, a missing zero fill),
+builds the variant with gcc in a temporary directory and runs every pin of
+tests/pins.py against it in a child process.  The child must fail.  This is
+CPU-only and never touches the product library."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "gpb_oracle.c")
+
+MUTANTS = {
+    "slot0_not_reserved_src": ("src[s] = i + 1;", "src[s] = i;"),
+    "slot0_not_reserved_inverse": ("= w * CAP + i + 1;", "= w * CAP + i;"),
+    "current_base_drops_prefix": ("current_bases[r] = PS * run_slots + PS * prefix_pages[r];",
+                                  "current_bases[r] = PS * run_slots;"),
+    "q_starts_inclusive": ("q_starts[r] = run_tokens;",
+                           "q_starts[r] = run_tokens + cur_tokens[r];"),
+    "k_bases_in_pages": ("k_bases[r] = PS * run_slots;", "k_bases[r] = run_slots;"),
+    "q_bases_in_pages": ("q_bases[r] = PS * run_cur_pages;", "q_bases[r] = run_cur_pages;"),
+    "kv_lens_page_padded": ("kv_lens[r] = PS * prefix_pages[r] + cur_tokens[r];",
+                            "kv_lens[r] = PS * (prefix_pages[r] + C);"),
+    "owner_skips_pool_entries": ("owner[s] = NP + writer[i];", "owner[s] = writer[i];"),
+    "single_writer": ("int32_t w = i % W;", "int32_t w = 0;"),
+    "prefix_owner_not_modulo": ("owner[s] = slot_pages[s] % NP;", "owner[s] = 0;"),
+    "no_staging_zero": ("memset(staging, 0, (size_t)(n_staging_rows * RB));", ";"),
+    "sentinel_not_zeroed": ("if (e < 0 || p < 0) { memset(out, 0, (size_t)page_bytes); continue; }",
+                            "if (e < 0 || p < 0) { continue; }"),
+    "gather_row_stride": ("table[e] + (int64_t)p * page_bytes", "table[e] + (int64_t)p * RB"),
+    "floor_not_ceil": ("return (a + b - 1) / b;", "return a / b;"),
+    "dummy_page_accepted": ("if (p < 1 || p >= n_pool_pages || seen[p])",
+                            "if (p < 0 || p >= n_pool_pages || seen[p])"),
+    "duplicates_accepted": ("if (p < 1 || p >= n_pool_pages || seen[p])",
+                            "if (p < 1 || p >= n_pool_pages)"),
+    "capacity_off_by_one": ("if (1 + total_cur_pages > staging_cap_pages)",
+                            "if (total_cur_pages > staging_cap_pages)"),
+    "token_page_index": ("int32_t s = slot_base[r] + prefix_pages[r] + j / PS;",
+                         "int32_t s = slot_base[r] + prefix_pages[r];"),
+    "prefix_span_end": ("prefix_span[2 * r + 1] = running_slots + prefix_pages[r];",
+                        "prefix_span[2 * r + 1] = running_slots + n;"),
+    "inverse_not_cleared": ("for (int32_t p = 0; p < n_pool_pages; p++) page_inverse[p] = -1;",
+                            ";"),
+    "mixed_locs_from_k_base": ("mixed_locs[t] = current_bases[r] + j;",
+                               "mixed_locs[t] = k_bases[r] + j;"),
+    "stray_row_not_flagged": ("if (row < 0 || row >= n_staging_rows) { bad = 1; continue; }",
+                              "if (row < 0 || row >= n_staging_rows) { continue; }"),
+}
+
+CHILD = r"""
+import os, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, pins
+try:
+    pins.run_all(oracle.Oracle({lib!r}), n_random=40)
+except AssertionError as e:
+    print("PIN FAILED:", e, flush=True)
+    os._exit(3)   # a mutant may have corrupted the heap: skip teardown
+except ValueError as e:
+    print("REJECTED A VALID BATCH:", e, flush=True)
+    os._exit(4)
+print("ALL PINS PASSED")
+"""
+
+
+def _build_variant(name, old, new, tmp):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, "mutation target not found: " + old
+    text = text.replace(old, new, 1)
+    c = os.path.join(tmp, name + ".c")
+    so = os.path.join(tmp, name + ".so")
+    open(c, "w").write(text)
+    subprocess.run(["gcc", "-O1", "-std=c11", "-w", "-shared", "-fPIC", "-o", so, c],
+                   check=True)
+    return so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTANTS[name]
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_variant(name, old, new, tmp)
+        code = CHILD.format(root=ROOT, tests=HERE, lib=so)
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                           text=True, timeout=300)
+    assert r.returncode in (3, 4), "planted mistake %s was not caught by a pin (rc %d):\n%s" % (
+        name, r.returncode, r.stdout[-2000:] + r.stderr[-2000:])
+
+
+def test_unmutated_oracle_passes_in_child():
+    code = CHILD.format(root=ROOT, tests=HERE,
+                        lib=os.path.join(ROOT, "oracle", "liboracle.so"))
+    import oracle
+    oracle.default()   # make sure the library is built
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
