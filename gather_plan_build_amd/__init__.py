@@ -1,0 +1,10 @@
+"""MI355X-native KV-compose hot path: per-batch plan build, per-layer current
+row scatter and slot-dense page gather (libgpb.so, HIP for gfx950).
+
+Importing this package loads libgpb.so and fails loudly if it is missing.
+"""
+from .binding import (BatchMeta, GpbError, Plan, Sources, compose_gather,  # noqa: F401
+                      current_row_scatter, plan_build, plan_sizes, staging_clear,
+                      strerror, LIB_PATH, PLAN_FIELDS, STATUS_BAD_DESCRIPTOR,
+                      STATUS_BAD_STAGING_ROW)
+from .runner import ComposeRunner  # noqa: F401

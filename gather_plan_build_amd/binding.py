@@ -1,0 +1,250 @@
+"""ctypes binding of libgpb.so (the C ABI in include/gpb.h).
+
+Argument marshalling only: every step of the compose path runs in the HIP
+kernels behind the C calls.  torch provides device memory and streams.  The
+functions keep the C names without the ``gpb_`` prefix.
+
+There is no fallback: if libgpb.so is missing or fails to load, importing this
+module raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("GPB_LIB", os.path.join(HERE, "libgpb.so"))
+
+MAX_SOURCES = 64
+STATUS_BAD_DESCRIPTOR = 1
+STATUS_BAD_STAGING_ROW = 2
+
+OK, EINVAL, EALIGN, EPAGE, ECAPACITY, ERANGE, EHIP = 0, -1, -2, -3, -4, -5, -6
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+class gpb_batch(ctypes.Structure):
+    _fields_ = [("bs", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int32), ("n_pool_pages", ctypes.c_int32),
+                ("n_pool_entries", ctypes.c_int32), ("n_writers", ctypes.c_int32),
+                ("staging_cap_pages", ctypes.c_int32),
+                ("h_prefix_pages", ctypes.c_void_p), ("h_cur_tokens", ctypes.c_void_p),
+                ("h_req_pages", ctypes.c_void_p), ("d_prefix_pages", ctypes.c_void_p),
+                ("d_cur_tokens", ctypes.c_void_p), ("d_req_pages", ctypes.c_void_p)]
+
+
+PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
+               "q_starts", "k_bases", "q_bases", "current_bases", "slot_pages",
+               "owner", "src", "page_inverse", "staging_page_inverse", "writer",
+               "staging_rows", "mixed_locs")
+
+
+class gpb_plan(ctypes.Structure):
+    _fields_ = [("d_" + f, ctypes.c_void_p) for f in PLAN_FIELDS]
+
+
+class gpb_sources(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32),
+                ("base", ctypes.c_void_p * MAX_SOURCES),
+                ("n_pages", ctypes.c_int64 * MAX_SOURCES)]
+
+
+def _hip_runtimes():
+    """Distinct libamdhip64 files mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1] if len(line.split()) >= 6 else ""
+                if "libamdhip64" in os.path.basename(path):
+                    found.add(os.path.realpath(path))
+    except OSError:
+        pass
+    return found
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise ImportError("libgpb.so not built at %s: run python -m "
+                          "gather_plan_build_amd.build (no fallback exists)" % path)
+    # torch provides device memory and streams; its HIP runtime must be the
+    # one libgpb.so binds to (same SONAME, loaded first), or the process would
+    # hold two runtimes whose streams and devices do not mix.
+    import torch  # noqa: F401
+    import torch.cuda  # noqa: F401
+    lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded (%s): load torch before "
+                          "libgpb.so" % ", ".join(sorted(runtimes)))
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.gpb_plan_sizes.argtypes = [ctypes.POINTER(gpb_batch), _I32P, _I32P, _I32P]
+    lib.gpb_plan_build.argtypes = [ctypes.POINTER(gpb_batch), ctypes.POINTER(gpb_plan), vp]
+    lib.gpb_staging_clear.argtypes = [vp, i64, vp]
+    lib.gpb_current_row_scatter.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp]
+    lib.gpb_compose_gather.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, vp, i32,
+                                       i32, i32, vp, vp]
+    lib.gpb_strerror.argtypes = [ctypes.c_int]
+    lib.gpb_strerror.restype = ctypes.c_char_p
+    for f in ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
+              "gpb_current_row_scatter", "gpb_compose_gather"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+lib = _load(LIB_PATH)
+
+EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
+           "gpb_current_row_scatter", "gpb_compose_gather", "gpb_strerror")
+
+
+class GpbError(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__("%s: %s (%d)" % (what, strerror(code), code))
+
+
+def strerror(code):
+    return lib.gpb_strerror(int(code)).decode()
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise GpbError(rc, what)
+
+
+def _ptr(x):
+    """Device address of a torch tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _host_i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
+
+
+class BatchMeta:
+    """Host side of a gpb_batch: geometry plus the three host arrays."""
+
+    def __init__(self, bs, page_size, row_bytes, n_pool_pages, n_pool_entries,
+                 n_writers, staging_cap_pages, prefix_pages, cur_tokens, req_pages):
+        self.h_prefix = _host_i32(prefix_pages)
+        self.h_cur = _host_i32(cur_tokens)
+        self.h_req = _host_i32(req_pages)
+        self.c = gpb_batch(bs, page_size, row_bytes, n_pool_pages, n_pool_entries,
+                           n_writers, staging_cap_pages,
+                           self.h_prefix.ctypes.data if self.h_prefix.size else None,
+                           self.h_cur.ctypes.data if self.h_cur.size else None,
+                           self.h_req.ctypes.data if self.h_req.size else None,
+                           None, None, None)
+
+    @classmethod
+    def of(cls, b):
+        """From any object with the workload attributes (workloads.Batch)."""
+        return cls(b.bs, b.page_size, b.row_bytes, b.n_pool_pages, b.n_pool_entries,
+                   b.n_writers, b.staging_cap_pages, b.prefix_pages, b.cur_tokens,
+                   b.req_pages)
+
+
+def plan_sizes(meta):
+    """(S, T, NCP) after host validation; raises GpbError on a bad batch."""
+    S, T, NCP = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.gpb_plan_sizes(ctypes.byref(meta.c), ctypes.byref(S), ctypes.byref(T),
+                              ctypes.byref(NCP)), "gpb_plan_sizes")
+    return S.value, T.value, NCP.value
+
+
+class Plan:
+    """Device inputs and outputs of gpb_plan_build for one batch.
+
+    Construction validates the batch on the host, copies the three metadata
+    arrays to the device once and allocates every output (torch int32).
+    ``build`` launches the plan kernels; the outputs are ``self.t[name]``."""
+
+    def __init__(self, meta, device="cuda"):
+        import torch
+        self.meta = meta
+        self.S, self.T, self.NCP = plan_sizes(meta)
+        b = meta.c
+        dev = torch.device(device)
+        self.d_prefix = torch.from_numpy(meta.h_prefix).to(dev)
+        self.d_cur = torch.from_numpy(meta.h_cur).to(dev)
+        self.d_req = torch.from_numpy(meta.h_req).to(dev)
+        b.d_prefix_pages = self.d_prefix.data_ptr() if self.d_prefix.numel() else None
+        b.d_cur_tokens = self.d_cur.data_ptr() if self.d_cur.numel() else None
+        b.d_req_pages = self.d_req.data_ptr() if self.d_req.numel() else None
+        bs, npp = b.bs, b.n_pool_pages
+        sizes = {"slot_base": bs, "prefix_span": 2 * bs, "current_span": 2 * bs,
+                 "q_lens": bs, "kv_lens": bs, "q_starts": bs, "k_bases": bs,
+                 "q_bases": bs, "current_bases": bs, "slot_pages": self.S,
+                 "owner": self.S, "src": self.S, "page_inverse": npp,
+                 "staging_page_inverse": npp, "writer": self.NCP,
+                 "staging_rows": self.T, "mixed_locs": self.T}
+        self.t = {k: torch.empty(sizes[k], dtype=torch.int32, device=dev)
+                  for k in PLAN_FIELDS}
+        self.c = gpb_plan(*[(self.t[k].data_ptr() if sizes[k] else None)
+                            for k in PLAN_FIELDS])
+
+    def build(self, stream=None):
+        _check(lib.gpb_plan_build(ctypes.byref(self.meta.c), ctypes.byref(self.c),
+                                  _stream(stream)), "gpb_plan_build")
+        return self
+
+
+def plan_build(meta, device="cuda", stream=None):
+    """Validate, allocate and launch: returns the Plan (outputs in .t)."""
+    return Plan(meta, device).build(stream)
+
+
+class Sources:
+    """A gpb_sources pointer table: [(base, n_pages), ...] with base a tensor
+    or a device address.  Built once, passed by reference to every gather."""
+
+    def __init__(self, entries):
+        if not 1 <= len(entries) <= MAX_SOURCES:
+            raise GpbError(EINVAL, "Sources")
+        self.keep = [e[0] for e in entries]
+        self.c = gpb_sources()
+        self.c.n = len(entries)
+        for i, (base, n_pages) in enumerate(entries):
+            self.c.base[i] = _ptr(base)
+            self.c.n_pages[i] = int(n_pages)
+
+
+def staging_clear(buf, n_bytes=None, stream=None):
+    """Zero a staging region (tensor, or address with n_bytes)."""
+    if n_bytes is None:
+        n_bytes = buf.numel() * buf.element_size()
+    _check(lib.gpb_staging_clear(_ptr(buf), int(n_bytes), _stream(stream)),
+           "gpb_staging_clear")
+
+
+def current_row_scatter(staging, n_staging_rows, staging_rows, cur_rows, n_rows,
+                        row_bytes, status=None, stream=None):
+    _check(lib.gpb_current_row_scatter(_ptr(staging), int(n_staging_rows),
+                                       _ptr(staging_rows), _ptr(cur_rows), int(n_rows),
+                                       int(row_bytes), _ptr(status), _stream(stream)),
+           "gpb_current_row_scatter")
+
+
+def compose_gather(dense, sources, owner, src, n_slots, page_rows, row_bytes,
+                   status=None, stream=None):
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_gather(_ptr(dense), ctypes.byref(sources.c), _ptr(owner),
+                                  _ptr(src), int(n_slots), int(page_rows),
+                                  int(row_bytes), _ptr(status), _stream(stream)),
+           "gpb_compose_gather")

@@ -1,0 +1,271 @@
+// compose.hip -- per-layer current-row scatter and slot-dense page gather,
+// plus the per-batch staging clear (gfx950).
+//
+// Page d63fbd4, commit "current rows written straight into staging": per
+// layer, one index_copy_ of the current token rows into the zeroed staging
+// span, then ONE gather that fills every dense slot with a whole page from a
+// [pool entries || staging entries] pointer table (prefix slots read the
+// pool, current slots read staging slot i + 1 of their writer).  Page
+// d63fbd4, commit "compose_v2": -1 descriptors zero-fill.  Page 0d87bc5,
+// commit "fp8 index_copy_ -> uint8 views": rows are opaque bytes.
+//
+// Both per-layer kernels are HBM-bound copies.  Every lane moves 16-byte
+// chunks (buffer_load_dwordx4 / buffer_store_dwordx4), issues all of its
+// loads before its first store so several are in flight, and marks the
+// traffic non-temporal: each byte is read once and written once per layer.
+#include <algorithm>
+#include <cstdio>
+
+#include "gpb_common.h"
+
+#ifndef GPB_GATHER_CPT
+#define GPB_GATHER_CPT 0   // 0: chosen per shape at launch
+#endif
+#ifndef GPB_SCATTER_CPT
+#define GPB_SCATTER_CPT 8
+#endif
+
+namespace gpb {
+namespace {
+
+struct SrcTable {
+  const uint8_t *base[GPB_MAX_SOURCES];
+  int64_t n_pages[GPB_MAX_SOURCES];
+  int32_t n;
+};
+
+// Raw buffer resources: a base address plus a byte range the hardware checks
+// on every access.  A load outside the range returns zeros and a store
+// outside it is dropped, so ragged tails, -1 sentinels and bad rows need no
+// branches around the memory instructions (branches around them would make
+// the compiler wait for each store before the next).
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw addressing
+constexpr int kNonTemporal = 2;         // each byte is touched once per layer
+constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every range we build
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
+}
+
+// One workgroup per (slot, part).  The slot's descriptor is uniform across
+// the workgroup: owner/src are scalar loads and both buffer resources live in
+// scalar registers.  Lane l moves chunks l, l + 256, ... of the part, so each
+// wave's access is one contiguous 1 KiB run.  An invalid or -1 descriptor
+// gets a source range of 0 bytes: every load returns zeros.
+template <int CPT>
+__global__ __launch_bounds__(kBlock) void k_compose_gather(
+    uint8_t *__restrict__ dense, SrcTable tbl, const int32_t *__restrict__ owner,
+    const int32_t *__restrict__ src, int32_t page_bytes, int32_t parts,
+    int32_t *status) {
+  const int slot = blockIdx.x / parts;
+  const int part = blockIdx.x - slot * parts;
+  const int e = owner[slot];
+  const int p = src[slot];
+  const bool sentinel = (e < 0) || (p < 0);
+  const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
+  const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(dense + static_cast<int64_t>(slot) * page_bytes, page_bytes);
+  const uint32_t first = (static_cast<uint32_t>(part) * (kBlock * CPT) + threadIdx.x) * 16u;
+  u32x4 v[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) v[k] = ld16(rs, first + k * (kBlock * 16));
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) st16(v[k], rd, first + k * (kBlock * 16));
+  if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
+    atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+}
+
+// Flat over (row, chunk) of the current rows: lane g of the grid handles
+// chunks g, g + 256, ... of its workgroup's range; the (row, offset) pair
+// advances by the precomputed (256 div row_chunks, 256 mod row_chunks), so a
+// lane divides once.  Consecutive lanes read consecutive source chunks; the
+// destination row of each chunk comes from staging_rows.  Chunks past the
+// last row read zeros and their stores go to kDropOffset (dropped), as do
+// rows whose staging row is out of range.
+template <int CPT>
+__global__ __launch_bounds__(kBlock) void k_row_scatter(
+    uint8_t *__restrict__ staging, int32_t staging_bytes, int32_t n_staging_rows,
+    const int32_t *__restrict__ rows, const uint8_t *__restrict__ cur,
+    int32_t n_rows, int32_t row_chunks, int32_t step_rows, int32_t step_off,
+    int32_t *status) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc(cur, n_rows * row_chunks * 16);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(staging, staging_bytes);
+  const int g = blockIdx.x * (kBlock * CPT) + threadIdx.x;
+  int row = g / row_chunks;
+  int off = g - row * row_chunks;
+  u32x4 v[CPT];
+  uint32_t dst[CPT];
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const bool live = row < n_rows;
+    const int d = rows[live ? row : n_rows - 1];
+    const bool ok = live && d >= 0 && d < n_staging_rows;
+    bad |= live && !ok;
+    v[k] = ld16(rs, static_cast<uint32_t>(row * row_chunks + off) * 16u);
+    dst[k] = ok ? static_cast<uint32_t>(d * row_chunks + off) * 16u : kDropOffset;
+    off += step_off;
+    row += step_rows;
+    if (off >= row_chunks) {
+      off -= row_chunks;
+      ++row;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) st16(v[k], rd, dst[k]);
+  if (bad && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill_zero(u32x4 *__restrict__ p,
+                                                      int64_t n_chunks) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+       i < n_chunks; i += stride)
+    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, p + i);
+}
+
+// Chunks per lane for a page of `page_chunks` chunks: the candidate that
+// wastes the fewest lane slots in the last part, then the larger unit.
+int pick_gather_cpt(int64_t page_chunks) {
+  if (GPB_GATHER_CPT > 0) return GPB_GATHER_CPT;
+  static const int cand[] = {16, 12, 9, 8, 6, 4};
+  int best = cand[0];
+  int64_t best_waste = INT64_MAX;
+  for (int c : cand) {
+    const int64_t unit = static_cast<int64_t>(kBlock) * c;
+    const int64_t waste = ceil_div64(page_chunks, unit) * unit - page_chunks;
+    if (waste < best_waste) {
+      best = c;
+      best_waste = waste;
+    }
+  }
+  return best;
+}
+
+template <int CPT>
+int launch_gather(uint8_t *dense, const SrcTable &t, const int32_t *owner,
+                  const int32_t *src, int32_t n_slots, int32_t page_chunks,
+                  int32_t *status, hipStream_t st) {
+  const int64_t parts = ceil_div64(page_chunks, static_cast<int64_t>(kBlock) * CPT);
+  const int64_t grid = parts * n_slots;
+  if (grid > INT32_MAX) return GPB_ERANGE;
+  return launch(k_compose_gather<CPT>, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
+                st, dense, t, owner, src, page_chunks * 16, parts, status);
+}
+
+}  // namespace
+}  // namespace gpb
+
+extern "C" int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream) {
+  using namespace gpb;
+  if (n_bytes < 0) return GPB_EINVAL;
+  if (n_bytes == 0) return GPB_OK;
+  if (!d_ptr) return GPB_EINVAL;
+  if (n_bytes % 16 != 0 || !aligned(d_ptr, 16)) return GPB_EALIGN;
+  const int64_t chunks = n_bytes / 16;
+  const int64_t grid = std::min<int64_t>(ceil_div64(chunks, kBlock * 4), 4096);
+  return launch(k_fill_zero, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
+                as_stream(stream), static_cast<u32x4 *>(d_ptr), chunks);
+}
+
+extern "C" int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
+                                       const int32_t *d_staging_rows,
+                                       const void *d_cur_rows, int32_t n_rows,
+                                       int32_t row_bytes, int32_t *d_status,
+                                       void *stream) {
+  using namespace gpb;
+  constexpr int CPT = GPB_SCATTER_CPT;
+  if (n_rows < 0 || n_staging_rows < 0 || row_bytes < 1) return GPB_EINVAL;
+  if (n_staging_rows > INT32_MAX) return GPB_ERANGE;
+  if (row_bytes % 16 != 0) return GPB_EALIGN;
+  if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
+  if (n_rows == 0) return GPB_OK;
+  if (!d_staging || !d_staging_rows || !d_cur_rows) return GPB_EINVAL;
+  if (!aligned(d_staging, 16) || !aligned(d_cur_rows, 16) || !aligned(d_staging_rows, 4))
+    return GPB_EALIGN;
+  const int64_t row_chunks = row_bytes / 16;
+  // buffer ranges are 32-bit byte counts: both regions must stay below 2 GiB
+  const int64_t cur_bytes = static_cast<int64_t>(n_rows) * row_bytes;
+  const int64_t staging_bytes = n_staging_rows * row_bytes;
+  if (cur_bytes > INT32_MAX || staging_bytes > INT32_MAX) return GPB_ERANGE;
+  const int64_t total = static_cast<int64_t>(n_rows) * row_chunks;
+  const int64_t grid = ceil_div64(total, static_cast<int64_t>(kBlock) * CPT);
+  return launch(k_row_scatter<CPT>, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
+                as_stream(stream), d_staging, staging_bytes, n_staging_rows,
+                d_staging_rows, d_cur_rows, n_rows, row_chunks, kBlock / row_chunks,
+                kBlock % row_chunks, d_status);
+}
+
+extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
+                                  const int32_t *d_owner, const int32_t *d_src,
+                                  int32_t n_slots, int32_t page_rows,
+                                  int32_t row_bytes, int32_t *d_status,
+                                  void *stream) {
+  using namespace gpb;
+  if (!table || n_slots < 0 || page_rows < 1 || row_bytes < 1) return GPB_EINVAL;
+  if (table->n < 1 || table->n > GPB_MAX_SOURCES) return GPB_EINVAL;
+  if (row_bytes % 16 != 0) return GPB_EALIGN;
+  if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
+  const int64_t page_chunks = static_cast<int64_t>(page_rows) * (row_bytes / 16);
+  // a page is one buffer range: 32-bit byte count
+  if (page_chunks * 16 > INT32_MAX - 16 * kBlock * 16) return GPB_ERANGE;
+  SrcTable t;
+  t.n = table->n;
+  for (int e = 0; e < GPB_MAX_SOURCES; ++e) {
+    t.base[e] = nullptr;
+    t.n_pages[e] = 0;
+  }
+  for (int e = 0; e < table->n; ++e) {
+    if (table->n_pages[e] < 0) return GPB_EINVAL;
+    if (table->n_pages[e] > 0 && !table->base[e]) return GPB_EINVAL;
+    if (!aligned(table->base[e], 16)) return GPB_EALIGN;
+    t.base[e] = static_cast<const uint8_t *>(table->base[e]);
+    t.n_pages[e] = table->n_pages[e];
+  }
+  if (n_slots == 0) return GPB_OK;
+  if (!d_dense || !d_owner || !d_src) return GPB_EINVAL;
+  if (!aligned(d_dense, 16) || !aligned(d_owner, 4) || !aligned(d_src, 4)) return GPB_EALIGN;
+  uint8_t *dense = static_cast<uint8_t *>(d_dense);
+  hipStream_t st = as_stream(stream);
+  const int32_t pc = static_cast<int32_t>(page_chunks);
+  switch (pick_gather_cpt(page_chunks)) {
+    case 4: return launch_gather<4>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 6: return launch_gather<6>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 8: return launch_gather<8>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 9: return launch_gather<9>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 12: return launch_gather<12>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 16: return launch_gather<16>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    default: return GPB_EINVAL;
+  }
+}
+
+namespace gpb {
+namespace {
+thread_local char hip_error_text[160] = "HIP launch failed";
+}  // namespace
+
+void note_hip_error(hipError_t e) {
+  snprintf(hip_error_text, sizeof(hip_error_text), "HIP launch failed: %s (%d)",
+           hipGetErrorString(e), static_cast<int>(e));
+}
+}  // namespace gpb
+
+extern "C" const char *gpb_strerror(int status) {
+  switch (status) {
+    case GPB_OK: return "ok";
+    case GPB_EINVAL: return "invalid argument";
+    case GPB_EALIGN: return "misaligned row size or pointer";
+    case GPB_EPAGE: return "page id is the dummy page 0, out of range, or repeated";
+    case GPB_ECAPACITY: return "staging capacity exceeded (slot 0 plus current pages)";
+    case GPB_ERANGE: return "index or size does not fit in int32";
+    case GPB_EHIP: return gpb::hip_error_text;
+    default: return "unknown gpb status";
+  }
+}

@@ -1,0 +1,288 @@
+// plan.hip -- per-batch plan build for the KV compose (gfx950).
+//
+// Page d63fbd4, commit "current rows written straight into staging": the
+// plan carries a staging-remapped page inverse that retargets the fill, and
+// the layer-invariant mixed_locs / staging row indices are built once per
+// batch.  Page d63fbd4, commit "cut per-layer CPU on the prefill launch
+// path": the ragged int32 descriptors and slot spans come from batch
+// metadata only, with no device synchronisation.  Page 0d87bc5, commit
+// "prefetch staging exchange": page 0 is the dummy page and the staging slot
+// of current page i is i + 1.
+//
+// Three launches on the caller's stream, each a plain function of the
+// previous one's outputs:
+//   1. k_plan_scan_fill: workgroup 0 runs wave-level exclusive scans over the
+//      per-request counts (slots n, tokens c, current pages C) and writes the
+//      spans and ragged descriptors; the other workgroups fill both page
+//      inverses with -1.
+//   2. k_plan_slots: one lane per dense slot -> slot page, page inverse,
+//      gather descriptor, writer and staging page inverse.
+//   3. k_plan_tokens: one lane per current token -> staging row through the
+//      staging page inverse, and mixed_locs.
+// Request lookups in 2 and 3 are binary searches over the scanned bases,
+// staged in LDS.
+#include <algorithm>
+#include <vector>
+
+#include "gpb_common.h"
+
+namespace gpb {
+namespace {
+
+constexpr int kLdsRequests = 1024;  // requests whose bases fit the LDS stage
+
+struct PlanArgs {
+  int32_t bs, ps, np, w, cap, n_pool_pages, n_slots, n_rows;
+  const int32_t *P, *c, *req_pages;
+  int32_t *slot_base, *prefix_span, *current_span;
+  int32_t *q_lens, *kv_lens, *q_starts, *k_bases, *q_bases, *current_bases;
+  int32_t *slot_pages, *owner, *src, *page_inverse, *staging_page_inverse;
+  int32_t *writer, *staging_rows, *mixed_locs;
+};
+
+// Inclusive scan across one wave64 (Hillis-Steele over lane shuffles).
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ void scan_requests(const PlanArgs &a) {
+  __shared__ int wave_tot[3][kBlock / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry_n = 0, carry_c = 0, carry_C = 0;
+  for (int base = 0; base < a.bs; base += kBlock) {
+    const int r = base + tid;
+    int P = 0, c = 0;
+    if (r < a.bs) {
+      P = a.P[r];
+      c = a.c[r];
+    }
+    const int C = (c + a.ps - 1) / a.ps;
+    const int n = P + C;
+    const int in_n = wave_inclusive_scan(n, lane);
+    const int in_c = wave_inclusive_scan(c, lane);
+    const int in_C = wave_inclusive_scan(C, lane);
+    if (lane == 63) {
+      wave_tot[0][wave] = in_n;
+      wave_tot[1][wave] = in_c;
+      wave_tot[2][wave] = in_C;
+    }
+    __syncthreads();
+    int pre_n = carry_n, pre_c = carry_c, pre_C = carry_C;
+    int all_n = carry_n, all_c = carry_c, all_C = carry_C;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) {
+      if (w < wave) {
+        pre_n += wave_tot[0][w];
+        pre_c += wave_tot[1][w];
+        pre_C += wave_tot[2][w];
+      }
+      all_n += wave_tot[0][w];
+      all_c += wave_tot[1][w];
+      all_C += wave_tot[2][w];
+    }
+    if (r < a.bs) {
+      const int ex_n = pre_n + in_n - n;  // exclusive sums
+      const int ex_c = pre_c + in_c - c;
+      const int ex_C = pre_C + in_C - C;
+      a.slot_base[r] = ex_n;
+      a.prefix_span[2 * r] = ex_n;
+      a.prefix_span[2 * r + 1] = ex_n + P;
+      a.current_span[2 * r] = ex_n + P;
+      a.current_span[2 * r + 1] = ex_n + n;
+      a.q_lens[r] = c;
+      a.kv_lens[r] = a.ps * P + c;
+      a.q_starts[r] = ex_c;
+      a.k_bases[r] = a.ps * ex_n;
+      a.current_bases[r] = a.ps * (ex_n + P);
+      a.q_bases[r] = a.ps * ex_C;
+    }
+    carry_n = all_n;
+    carry_c = all_c;
+    carry_C = all_C;
+    __syncthreads();  // wave_tot is reused by the next tile
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_plan_scan_fill(PlanArgs a) {
+  if (blockIdx.x == 0) {
+    scan_requests(a);
+    return;
+  }
+  const int stride = (gridDim.x - 1) * kBlock;
+  for (int p = (blockIdx.x - 1) * kBlock + threadIdx.x; p < a.n_pool_pages; p += stride) {
+    a.page_inverse[p] = -1;
+    a.staging_page_inverse[p] = -1;
+  }
+}
+
+// Largest r in [0, bs) with base[r] <= x, given base[0] == 0 <= x and base
+// non-decreasing.  Requests with no entries share the next request's base and
+// are skipped because the search keeps the last equal base.
+__device__ __forceinline__ int find_request(const int32_t *base, int bs, int x) {
+  int lo = 0, hi = bs;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (base[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
+  __shared__ int32_t s_base[kLdsRequests], s_P[kLdsRequests], s_qb[kLdsRequests];
+  const bool lds = a.bs <= kLdsRequests;
+  if (lds) {
+    for (int r = threadIdx.x; r < a.bs; r += kBlock) {
+      s_base[r] = a.slot_base[r];
+      s_P[r] = a.P[r];
+      s_qb[r] = a.q_bases[r];
+    }
+    __syncthreads();
+  }
+  const int32_t *base = lds ? s_base : a.slot_base;
+  const int32_t *Pv = lds ? s_P : a.P;
+  const int32_t *qb = lds ? s_qb : a.q_bases;
+  const int s = blockIdx.x * kBlock + threadIdx.x;
+  if (s >= a.n_slots) return;
+  const int r = find_request(base, a.bs, s);
+  const int j = s - base[r];
+  const int P = Pv[r];
+  const int page = a.req_pages[s];
+  a.slot_pages[s] = page;
+  a.page_inverse[page] = s;
+  if (j < P) {  // prefix slot: modulo-owned pool entry, the page itself
+    a.owner[s] = page % a.np;
+    a.src[s] = page;
+  } else {      // current page i of the batch
+    const int i = qb[r] / a.ps + (j - P);
+    const int w = i % a.w;
+    a.writer[i] = w;
+    a.owner[s] = a.np + w;
+    a.src[s] = i + 1;
+    a.staging_page_inverse[page] = w * a.cap + i + 1;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
+  __shared__ int32_t s_qs[kLdsRequests], s_base[kLdsRequests], s_P[kLdsRequests],
+      s_cb[kLdsRequests];
+  const bool lds = a.bs <= kLdsRequests;
+  if (lds) {
+    for (int r = threadIdx.x; r < a.bs; r += kBlock) {
+      s_qs[r] = a.q_starts[r];
+      s_base[r] = a.slot_base[r];
+      s_P[r] = a.P[r];
+      s_cb[r] = a.current_bases[r];
+    }
+    __syncthreads();
+  }
+  const int32_t *qs = lds ? s_qs : a.q_starts;
+  const int32_t *base = lds ? s_base : a.slot_base;
+  const int32_t *Pv = lds ? s_P : a.P;
+  const int32_t *cb = lds ? s_cb : a.current_bases;
+  const int t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= a.n_rows) return;
+  const int r = find_request(qs, a.bs, t);
+  const int j = t - qs[r];
+  const int s = base[r] + Pv[r] + j / a.ps;
+  const int loc = a.slot_pages[s] * a.ps + j % a.ps;  // the token's pool row
+  const int spage = a.staging_page_inverse[loc / a.ps];
+  a.staging_rows[t] = spage * a.ps + loc % a.ps;
+  a.mixed_locs[t] = cb[r] + j;
+}
+
+// Host-side validation of a batch; the rules and their order match the
+// header: shape, then sizes, then staging capacity, then page ids.
+int validate_batch(const gpb_batch *b, int32_t *S_out, int32_t *T_out,
+                   int32_t *NCP_out) {
+  if (!b) return GPB_EINVAL;
+  if (b->bs < 0 || b->page_size < 1 || b->n_pool_pages < 1 ||
+      b->n_pool_entries < 1 || b->n_writers < 1 || b->staging_cap_pages < 1 ||
+      b->row_bytes < 1)
+    return GPB_EINVAL;
+  if (b->row_bytes % 16 != 0) return GPB_EALIGN;
+  if (b->bs > 0 && (!b->h_prefix_pages || !b->h_cur_tokens)) return GPB_EINVAL;
+  int64_t S = 0, T = 0, NCP = 0;
+  for (int32_t r = 0; r < b->bs; ++r) {
+    const int64_t P = b->h_prefix_pages[r], c = b->h_cur_tokens[r];
+    if (P < 0 || c < 0) return GPB_EINVAL;
+    const int64_t C = ceil_div64(c, b->page_size);
+    S += P + C;
+    T += c;
+    NCP += C;
+  }
+  if (S * b->page_size > INT32_MAX || T > INT32_MAX ||
+      static_cast<int64_t>(b->n_pool_pages) * b->page_size > INT32_MAX ||
+      static_cast<int64_t>(b->n_writers) * b->staging_cap_pages * b->page_size > INT32_MAX)
+    return GPB_ERANGE;
+  if (1 + NCP > b->staging_cap_pages) return GPB_ECAPACITY;
+  if (S > 0 && !b->h_req_pages) return GPB_EINVAL;
+  std::vector<uint8_t> seen(static_cast<size_t>(b->n_pool_pages), 0);
+  for (int64_t k = 0; k < S; ++k) {
+    const int32_t p = b->h_req_pages[k];
+    if (p < 1 || p >= b->n_pool_pages || seen[p]) return GPB_EPAGE;
+    seen[p] = 1;
+  }
+  if (S_out) *S_out = static_cast<int32_t>(S);
+  if (T_out) *T_out = static_cast<int32_t>(T);
+  if (NCP_out) *NCP_out = static_cast<int32_t>(NCP);
+  return GPB_OK;
+}
+
+bool ok_array(const void *p, int64_t n) { return n == 0 || (p && aligned(p, 4)); }
+
+}  // namespace
+}  // namespace gpb
+
+extern "C" int gpb_plan_sizes(const gpb_batch *batch, int32_t *n_slots,
+                              int32_t *n_rows, int32_t *n_cur_pages) {
+  return gpb::validate_batch(batch, n_slots, n_rows, n_cur_pages);
+}
+
+extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *stream) {
+  using namespace gpb;
+  int32_t S = 0, T = 0, NCP = 0;
+  int rc = validate_batch(b, &S, &T, &NCP);
+  if (rc != GPB_OK) return rc;
+  if (!o) return GPB_EINVAL;
+  const int64_t bs = b->bs, npp = b->n_pool_pages;
+  struct Need { const void *p; int64_t n; };
+  const Need need[] = {
+      {b->d_prefix_pages, bs}, {b->d_cur_tokens, bs}, {b->d_req_pages, S},
+      {o->d_slot_base, bs}, {o->d_prefix_span, 2 * bs}, {o->d_current_span, 2 * bs},
+      {o->d_q_lens, bs}, {o->d_kv_lens, bs}, {o->d_q_starts, bs},
+      {o->d_k_bases, bs}, {o->d_q_bases, bs}, {o->d_current_bases, bs},
+      {o->d_slot_pages, S}, {o->d_owner, S}, {o->d_src, S},
+      {o->d_page_inverse, npp}, {o->d_staging_page_inverse, npp},
+      {o->d_writer, NCP}, {o->d_staging_rows, T}, {o->d_mixed_locs, T}};
+  for (const Need &e : need) {
+    if (e.n > 0 && !e.p) return GPB_EINVAL;
+    if (!ok_array(e.p, e.n)) return GPB_EALIGN;
+  }
+  PlanArgs a;
+  a.bs = b->bs; a.ps = b->page_size; a.np = b->n_pool_entries; a.w = b->n_writers;
+  a.cap = b->staging_cap_pages; a.n_pool_pages = b->n_pool_pages;
+  a.n_slots = S; a.n_rows = T;
+  a.P = b->d_prefix_pages; a.c = b->d_cur_tokens; a.req_pages = b->d_req_pages;
+  a.slot_base = o->d_slot_base; a.prefix_span = o->d_prefix_span;
+  a.current_span = o->d_current_span; a.q_lens = o->d_q_lens; a.kv_lens = o->d_kv_lens;
+  a.q_starts = o->d_q_starts; a.k_bases = o->d_k_bases; a.q_bases = o->d_q_bases;
+  a.current_bases = o->d_current_bases; a.slot_pages = o->d_slot_pages;
+  a.owner = o->d_owner; a.src = o->d_src; a.page_inverse = o->d_page_inverse;
+  a.staging_page_inverse = o->d_staging_page_inverse; a.writer = o->d_writer;
+  a.staging_rows = o->d_staging_rows; a.mixed_locs = o->d_mixed_locs;
+
+  hipStream_t st = as_stream(stream);
+  // workgroup 0 scans; the rest fill the inverses (4 entries per lane-pass)
+  const int64_t fill_blocks = std::min<int64_t>(256, ceil_div64(npp, kBlock * 4));
+  rc = launch(k_plan_scan_fill, dim3(1 + fill_blocks), dim3(kBlock), st, a);
+  if (rc == GPB_OK && S > 0)
+    rc = launch(k_plan_slots, dim3(ceil_div64(S, kBlock)), dim3(kBlock), st, a);
+  if (rc == GPB_OK && T > 0)
+    rc = launch(k_plan_tokens, dim3(ceil_div64(T, kBlock)), dim3(kBlock), st, a);
+  return rc;
+}

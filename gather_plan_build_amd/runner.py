@@ -1,0 +1,109 @@
+"""The per-batch / per-layer compose loop on one GPU.
+
+Once per batch: build the plan and clear both staging halves.  Per layer l:
+scatter the layer's current rows into staging half l mod 2, then gather every
+dense slot into dense half l mod 2 through the [pool entries || staging slabs]
+table of that layer (page d63fbd4, commit "current rows written straight into
+staging": one index_copy_ into the zeroed staging span, then ONE slot-dense
+gather; the parity halves keep a layer's buffers from being overwritten by the
+next one, page d63fbd4, commit "touched-pages-proportional staging").
+
+On one GPU every pool entry of the table is the layer's own pool arena and
+every staging entry is a slab carved from the local staging region; stream
+order replaces the cross-GPU barrier.
+"""
+import torch
+
+from . import binding as B
+
+PARITY = 2
+
+
+class ComposeRunner:
+    """Arenas, plan and pointer tables for one batch.
+
+    pools[k], curs[k]: uint8 device tensors [rows, row_bytes]; layer l uses
+    index l mod len(pools)."""
+
+    def __init__(self, meta, pools, curs, device="cuda"):
+        b = meta.c
+        self.meta = meta
+        self.ps, self.rb = b.page_size, b.row_bytes
+        self.np_, self.w, self.cap = b.n_pool_entries, b.n_writers, b.staging_cap_pages
+        self.n_pool_pages = b.n_pool_pages
+        self.plan = B.Plan(meta, device)
+        self.S, self.T = self.plan.S, self.plan.T
+        self.pools, self.curs = list(pools), list(curs)
+        for p in self.pools:
+            assert p.dtype == torch.uint8 and p.is_contiguous()
+            assert p.numel() == self.n_pool_pages * self.ps * self.rb
+        for c in self.curs:
+            assert c.dtype == torch.uint8 and c.is_contiguous()
+            assert c.numel() == self.T * self.rb
+        self.staging_rows_total = self.w * self.cap * self.ps
+        slab = self.cap * self.ps * self.rb
+        dev = torch.device(device)
+        self.staging = [torch.empty(self.staging_rows_total * self.rb, dtype=torch.uint8,
+                                    device=dev) for _ in range(PARITY)]
+        self.dense = [torch.empty(max(self.S * self.ps * self.rb, 16), dtype=torch.uint8,
+                                  device=dev) for _ in range(PARITY)]
+        # buffers passed to the kernels must hold what the kernels address
+        assert self.staging[0].numel() >= self.staging_rows_total * self.rb
+        assert self.dense[0].numel() >= self.S * self.ps * self.rb
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.tables = {}
+        for k, pool in enumerate(self.pools):
+            for h in range(PARITY):
+                base = self.staging[h].data_ptr()
+                entries = [(pool, self.n_pool_pages)] * self.np_ + \
+                    [(base + w * slab, self.cap) for w in range(self.w)]
+                self.tables[(k, h)] = B.Sources(entries)
+
+    def begin_batch(self, stream=None):
+        """Plan build + clear of both staging halves (once per batch)."""
+        self.plan.build(stream)
+        for h in range(PARITY):
+            B.staging_clear(self.staging[h], stream=stream)
+
+    def scatter(self, layer, stream=None):
+        h, k = layer % PARITY, layer % len(self.curs)
+        B.current_row_scatter(self.staging[h], self.staging_rows_total,
+                              self.plan.t["staging_rows"], self.curs[k], self.T,
+                              self.rb, self.status, stream)
+
+    def gather(self, layer, stream=None):
+        h, k = layer % PARITY, layer % len(self.pools)
+        B.compose_gather(self.dense[h], self.tables[(k, h)], self.plan.t["owner"],
+                         self.plan.t["src"], self.S, self.ps, self.rb, self.status,
+                         stream)
+
+    def layer(self, layer, stream=None):
+        self.scatter(layer, stream)
+        self.gather(layer, stream)
+
+    def run(self, n_layers, stream=None):
+        self.begin_batch(stream)
+        for l in range(n_layers):
+            self.layer(l, stream)
+
+    def dense_of(self, layer):
+        """Dense half written by ``layer`` as [S*PS, RB] uint8 (valid until
+        layer + 2 runs)."""
+        return self.dense[layer % PARITY][:self.S * self.ps * self.rb].view(-1, self.rb)
+
+    def staging_of(self, layer):
+        return self.staging[layer % PARITY].view(-1, self.rb)
+
+    def algorithmic_bytes_per_layer(self):
+        """Bytes the compose must move per layer: read and write every dense
+        page, read and write every current row, plus the descriptor reads
+        (owner/src per slot, staging row per token) and the table."""
+        page = self.ps * self.rb
+        return (2 * self.S * page + 2 * self.T * self.rb + 8 * self.S + 4 * self.T
+                + 8 * (self.np_ + self.w))
+
+    def gather_bytes(self):
+        return 2 * self.S * self.ps * self.rb + 8 * self.S
+
+    def scatter_bytes(self):
+        return 2 * self.T * self.rb + 4 * self.T

@@ -1,0 +1,215 @@
+/*
+ * gpb.h -- C ABI of libgpb.so: the KV-compose hot path on one MI355X (gfx950).
+ *
+ * Per batch, gpb_plan_build turns host batch metadata into the layer-invariant
+ * plan: slot spans, the page inverse and its staging-remapped twin, gather
+ * descriptors (owner, src), per-token staging rows and mixed_locs, and the
+ * ragged int32 descriptors.  Per layer, gpb_current_row_scatter writes the
+ * current token rows into the zeroed staging span and gpb_compose_gather fills
+ * the slot-dense KV buffer one page per slot from a pointer table of source
+ * arenas [pool entries || staging slabs].
+ *
+ * Source of the method (commit pages of the sglang fork, by page and commit):
+ *   page d63fbd4, commit "current rows written straight into staging":
+ *     fill destinations come only from a page inverse, so a per-batch
+ *     staging-remapped inverse retargets the fill; the per-layer fill is one
+ *     index_copy_ into the zeroed staging span; ONE slot-dense gather over a
+ *     concatenated [pool || staging] pointer table, current slots carrying
+ *     owner = (number of pool entries) + writer and src = staging slot;
+ *     mixed_locs and staging row indices are built once per batch.
+ *   page d63fbd4, commit "touched-pages-proportional staging": staging holds
+ *     one round of current pages in merged-span order at slot = the page's
+ *     batch current index; overflow fails fast.
+ *   page d63fbd4, commit "compose_v2": descriptors of -1 zero-fill a slot.
+ *   page d63fbd4, commit "cut per-layer CPU on the prefill launch path":
+ *     the ragged int32 descriptors kv_lens/q_starts/q_lens/k_bases/q_bases/
+ *     current_bases and the slot spans, built once per batch from batch
+ *     metadata without device synchronisation.
+ *   page 0d87bc5, commit "prefetch staging exchange": page id 0 is the dummy
+ *     page; the staging slot of current page i is i + 1 (row block 0 unused).
+ *   page 0d87bc5, commit "canonical prefix/current slot spans": the spans are
+ *     the sole description of the prefix/current regions; an empty span is
+ *     valid, a missing one is an error.
+ *   page 0d87bc5, commit "fp8 index_copy_ -> uint8 views": rows are moved as
+ *     opaque bytes, whatever their element type.
+ *
+ * Conventions for every call:
+ *   - Returns GPB_OK (0) or a negative gpb_status.  Arguments are checked on
+ *     the host before anything is launched; a rejected call launches nothing
+ *     and leaves every output untouched.
+ *   - d_* pointers are device memory owned by the caller (for instance torch
+ *     tensors); h_* pointers are host memory read during the call only.  The
+ *     library allocates no device memory and never synchronises: every launch
+ *     is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     Order between calls is stream order; the caller keeps buffers alive
+ *     until the work is done.
+ *   - Row payloads are opaque bytes; row_bytes is a multiple of 16 and every
+ *     row-carrying pointer is 16-byte aligned.  Index arrays are int32 and
+ *     4-byte aligned; byte offsets are computed in 64 bits.
+ *   - Empty work (bs = 0, no slots, no rows) is valid and launches nothing
+ *     beyond what is needed to fill outputs that are not empty.
+ */
+#ifndef GPB_H
+#define GPB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gpb_status {
+  GPB_OK = 0,
+  GPB_EINVAL = -1,     /* null pointer where data is needed, negative size,
+                          geometry out of range, table with no entries      */
+  GPB_EALIGN = -2,     /* row_bytes % 16 != 0, or a pointer misaligned       */
+  GPB_EPAGE = -3,      /* a page id is 0 (dummy), >= n_pool_pages, or repeated
+                          within the batch                                   */
+  GPB_ECAPACITY = -4,  /* 1 + current pages > staging_cap_pages              */
+  GPB_ERANGE = -5,     /* a row or element index would not fit in int32     */
+  GPB_EHIP = -6        /* the HIP runtime refused a launch                   */
+} gpb_status;
+
+/* Bits the kernels OR into the optional device status word (int32). */
+#define GPB_STATUS_BAD_DESCRIPTOR 1  /* gather: owner >= table entries or src
+                                        >= that arena's pages; slot zeroed  */
+#define GPB_STATUS_BAD_STAGING_ROW 2 /* scatter: staging row < 0 or beyond
+                                        the staging region; row skipped      */
+
+#define GPB_MAX_SOURCES 64           /* pointer-table entries per gather    */
+
+/* Batch metadata for gpb_plan_build (page d63fbd4, commits "current rows
+ * written straight into staging" and "cut per-layer CPU on the prefill launch
+ * path").  Request r has prefix_pages[r] whole prefix pages (prefix lengths
+ * are page-aligned) and cur_tokens[r] current tokens, which occupy
+ * ceil(cur_tokens[r] / page_size) current pages.  req_pages lists, request by
+ * request, the pool page ids of its prefix pages then of its current pages;
+ * its length is sum over r of prefix_pages[r] + ceil(cur_tokens[r]/page_size).
+ * Every id is in [1, n_pool_pages) and distinct.  The host arrays are
+ * validated; the device arrays must hold the same values (the kernels read
+ * them, the host never reads device memory). */
+typedef struct gpb_batch {
+  int32_t bs;                   /* requests, >= 0                              */
+  int32_t page_size;            /* token rows per page, >= 1 (64)             */
+  int32_t row_bytes;            /* bytes per token row, multiple of 16        */
+  int32_t n_pool_pages;         /* pages per pool arena; page 0 = dummy       */
+  int32_t n_pool_entries;       /* NP: pool entries in the pointer table, >= 1 */
+  int32_t n_writers;            /* W: staging slabs, >= 1                     */
+  int32_t staging_cap_pages;    /* CAP: pages per slab, slot 0 included       */
+  const int32_t *h_prefix_pages;   /* host   [bs]                             */
+  const int32_t *h_cur_tokens;     /* host   [bs]                             */
+  const int32_t *h_req_pages;      /* host   [n_slots]                        */
+  const int32_t *d_prefix_pages;   /* device [bs], same values                */
+  const int32_t *d_cur_tokens;     /* device [bs], same values                */
+  const int32_t *d_req_pages;      /* device [n_slots], same values           */
+} gpb_batch;
+
+/* Caller-allocated plan outputs (int32, device).  Sizes from gpb_plan_sizes:
+ * S = n_slots, T = n_rows, NCP = n_cur_pages.  A pointer may be NULL only
+ * when its size is 0.  Definitions, for request r (C_r current pages,
+ * n_r = P_r + C_r slots; "exclusive sum" = sum over earlier requests):
+ *   slot_base[r]          exclusive sum of n                          [bs]
+ *   prefix_span[2r..2r+1] [slot_base, slot_base + P_r)                [2bs]
+ *   current_span[2r..]    [slot_base + P_r, slot_base + n_r)          [2bs]
+ *   q_lens[r]             c_r                                         [bs]
+ *   kv_lens[r]            page_size * P_r + c_r                       [bs]
+ *   q_starts[r]           exclusive sum of c (token-packed base)      [bs]
+ *   k_bases[r]            page_size * slot_base[r] (dense row base)   [bs]
+ *   current_bases[r]      k_bases[r] + page_size * P_r                [bs]
+ *   q_bases[r]            page_size * exclusive sum of C (page-padded
+ *                         current base)                               [bs]
+ *   slot_pages[s]         pool page held by dense slot s              [S]
+ *   owner[s], src[s]      gather descriptor: prefix slot -> pool entry
+ *                         (page mod NP), page; current page i (batch
+ *                         order) -> entry NP + writer(i), slot i + 1  [S]
+ *   page_inverse[p]       dense slot of pool page p, else -1   [n_pool_pages]
+ *   staging_page_inverse[p] carved staging page of current page p:
+ *                         writer*CAP + i + 1, else -1          [n_pool_pages]
+ *   writer[i]             i mod W (page-aligned round robin)          [NCP]
+ *   staging_rows[t]       staging row of current token t, found through
+ *                         staging_page_inverse                        [T]
+ *   mixed_locs[t]         dense row of current token t                [T]  */
+typedef struct gpb_plan {
+  int32_t *d_slot_base, *d_prefix_span, *d_current_span;
+  int32_t *d_q_lens, *d_kv_lens, *d_q_starts;
+  int32_t *d_k_bases, *d_q_bases, *d_current_bases;
+  int32_t *d_slot_pages, *d_owner, *d_src;
+  int32_t *d_page_inverse, *d_staging_page_inverse;
+  int32_t *d_writer;
+  int32_t *d_staging_rows, *d_mixed_locs;
+} gpb_plan;
+
+/* Pointer table of source arenas for one gather (page d63fbd4, commit
+ * "current rows written straight into staging": [pool entries || staging
+ * entries]).  Host struct; the library passes it to the kernel by value.
+ * base[e] is the device address of arena e (16-byte aligned), n_pages[e] the
+ * number of whole pages addressable from it.  On one GPU every pool entry is
+ * the layer's pool arena; staging entry w is slab w of the carved staging
+ * region, at d_staging + w * CAP * page_size * row_bytes. */
+typedef struct gpb_sources {
+  int32_t n;                                /* 1 .. GPB_MAX_SOURCES */
+  const void *base[GPB_MAX_SOURCES];
+  int64_t n_pages[GPB_MAX_SOURCES];
+} gpb_sources;
+
+/* Host only: validate the batch (every rule of gpb_plan_build) and return
+ * S (dense slots), T (current rows) and NCP (current pages).  Any of the
+ * output pointers may be NULL.  Reads only the h_* arrays. */
+int gpb_plan_sizes(const gpb_batch *batch, int32_t *n_slots, int32_t *n_rows,
+                   int32_t *n_cur_pages);
+
+/* Validate on the host, then launch the plan kernels on `stream`: a scan
+ * kernel (wave-level exclusive scans of the per-request counts, which also
+ * fills both page inverses with -1), a per-slot kernel (slot pages, page
+ * inverse, descriptors, writers, staging inverse) and a per-token kernel
+ * (staging rows through the staging inverse, mixed_locs).  The plan is
+ * layer-invariant: build it once per batch.  Errors: GPB_EINVAL, GPB_EPAGE,
+ * GPB_ECAPACITY, GPB_ERANGE (S*page_size, T, n_pool_pages*page_size or
+ * W*CAP*page_size beyond INT32_MAX), GPB_EALIGN (int32 arrays not 4-byte
+ * aligned), GPB_EHIP. */
+int gpb_plan_build(const gpb_batch *batch, const gpb_plan *plan, void *stream);
+
+/* Zero `n_bytes` bytes at d_ptr (n_bytes a multiple of 16, d_ptr 16-byte
+ * aligned): the per-batch clear of the staging region, so the rows of a last
+ * current page past its request's tokens read back as zero (page d63fbd4,
+ * commit "current rows written straight into staging": the fill writes into
+ * the zeroed staging span).  The staging rows a batch writes are the same in
+ * every layer, so one clear per batch serves all its layers.  A kernel, not a
+ * memset node, so the call can be captured in a HIP graph. */
+int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream);
+
+/* Per layer: staging row d_staging_rows[t] <- current row t, for t < n_rows,
+ * whole rows of row_bytes bytes (index_copy_ semantics on byte views: page
+ * d63fbd4, commit "current rows written straight into staging"; page
+ * 0d87bc5, commit "fp8 index_copy_ -> uint8 views").  d_cur_rows holds n_rows
+ * contiguous rows; d_staging holds n_staging_rows rows.  A staging row
+ * outside [0, n_staging_rows) is skipped and GPB_STATUS_BAD_STAGING_ROW is
+ * ORed into *d_status when d_status is not NULL (page 0d87bc5: index_copy_
+ * has no skip semantics for a stray -1, so the plan must never emit one).
+ * Rows must not repeat (the plan's rows are distinct). */
+int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
+                            const int32_t *d_staging_rows,
+                            const void *d_cur_rows, int32_t n_rows,
+                            int32_t row_bytes, int32_t *d_status,
+                            void *stream);
+
+/* Per layer: for every slot s < n_slots, dense page s (page_rows * row_bytes
+ * bytes at d_dense + s * page_rows * row_bytes) <- page d_src[s] of arena
+ * table->base[d_owner[s]]; a slot with d_owner[s] < 0 or d_src[s] < 0 is
+ * zero-filled (page d63fbd4, commit "compose_v2").  A descriptor with owner
+ * >= table->n or src >= table->n_pages[owner] is zero-filled as well and
+ * GPB_STATUS_BAD_DESCRIPTOR is ORed into *d_status when d_status is not NULL.
+ * The dense buffer must not overlap any source page it reads. */
+int gpb_compose_gather(void *d_dense, const gpb_sources *table,
+                       const int32_t *d_owner, const int32_t *d_src,
+                       int32_t n_slots, int32_t page_rows, int32_t row_bytes,
+                       int32_t *d_status, void *stream);
+
+/* Static, human-readable name of a gpb_status value. */
+const char *gpb_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPB_H */

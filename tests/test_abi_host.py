@@ -1,0 +1,177 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/gpb.h declares, and rejects bad arguments on the host before any
+launch (page d63fbd4, commit "touched-pages-proportional staging": overflow
+fails fast; page 0d87bc5, commit "prefetch staging exchange": page 0 is the
+dummy page).  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gather_plan_build_amd as gpb
+from gather_plan_build_amd import binding as B
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gpb.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(gpb_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert header_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gpb.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_names_every_status():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert gpb.strerror(code) and "unknown" not in gpb.strerror(code)
+    assert "unknown" in gpb.strerror(-99)
+
+
+def _meta(**kw):
+    base = dict(bs=2, page_size=64, row_bytes=1152, n_pool_pages=16, n_pool_entries=1,
+                n_writers=1, staging_cap_pages=4, prefix_pages=[1, 1], cur_tokens=[64, 65],
+                req_pages=[1, 2, 3, 4, 5])
+    base.update(kw)
+    return B.BatchMeta(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, B.OK),
+    (dict(req_pages=[0, 2, 3, 4, 5]), B.EPAGE),          # dummy page 0
+    (dict(req_pages=[1, 2, 3, 4, 1]), B.EPAGE),          # repeated page
+    (dict(req_pages=[1, 2, 3, 4, 16]), B.EPAGE),         # beyond the pool
+    (dict(req_pages=[1, 2, 3, 4, -2]), B.EPAGE),
+    (dict(staging_cap_pages=3), B.ECAPACITY),            # slot 0 + 3 pages
+    (dict(row_bytes=1000), B.EALIGN),
+    (dict(row_bytes=0), B.EINVAL),
+    (dict(page_size=0), B.EINVAL),
+    (dict(n_writers=0), B.EINVAL),
+    (dict(n_pool_entries=0), B.EINVAL),
+    (dict(prefix_pages=[1, -1]), B.EINVAL),
+    (dict(cur_tokens=[64, -3]), B.EINVAL),
+    (dict(bs=-1), B.EINVAL),
+    (dict(page_size=1 << 20, n_pool_pages=4096), B.ERANGE),
+])
+def test_plan_sizes_validation(kw, code):
+    m = _meta(**kw)
+    rc = B.lib.gpb_plan_sizes(ctypes.byref(m.c), None, None, None)
+    assert rc == code, gpb.strerror(rc)
+
+
+def test_empty_batch_is_valid():
+    m = B.BatchMeta(0, 64, 16, 8, 1, 1, 1, [], [], [])
+    assert gpb.plan_sizes(m) == (0, 0, 0)
+
+
+def test_plan_build_rejects_before_launch():
+    m = _meta(req_pages=[0, 2, 3, 4, 5])
+    p = B.gpb_plan()
+    assert B.lib.gpb_plan_build(ctypes.byref(m.c), ctypes.byref(p), None) == B.EPAGE
+    ok = _meta()
+    # valid batch but no device arrays / outputs: rejected on the host
+    assert B.lib.gpb_plan_build(ctypes.byref(ok.c), ctypes.byref(p), None) == B.EINVAL
+    assert B.lib.gpb_plan_build(ctypes.byref(ok.c), None, None) == B.EINVAL
+    assert B.lib.gpb_plan_build(None, ctypes.byref(p), None) == B.EINVAL
+
+
+def test_plan_build_rejects_misaligned_outputs():
+    m = _meta()
+    fake = 0x100000  # never dereferenced: the check fails before any launch
+    m.c.d_prefix_pages = fake
+    m.c.d_cur_tokens = fake
+    m.c.d_req_pages = fake
+    p = B.gpb_plan(*([fake] * len(B.PLAN_FIELDS)))
+    p.d_owner = fake + 2
+    assert B.lib.gpb_plan_build(ctypes.byref(m.c), ctypes.byref(p), None) == B.EALIGN
+
+
+def test_scatter_argument_checks():
+    f = B.lib.gpb_current_row_scatter
+    a = 0x100000
+    assert f(a, 10, a, a, 0, 1152, None, None) == B.OK          # empty: no launch
+    assert f(a, 10, a, a, -1, 1152, None, None) == B.EINVAL
+    assert f(a, 10, a, a, 4, 1000, None, None) == B.EALIGN
+    assert f(a + 8, 10, a, a, 4, 1152, None, None) == B.EALIGN
+    assert f(a, 10, a + 2, a, 4, 1152, None, None) == B.EALIGN
+    assert f(None, 10, a, a, 4, 1152, None, None) == B.EINVAL
+    assert f(a, 1 << 40, a, a, 4, 1152, None, None) == B.ERANGE
+    assert f(a, 10, a, a, 1 << 22, 1152, None, None) == B.ERANGE   # > 2 GiB of rows
+
+
+def test_gather_argument_checks():
+    f = B.lib.gpb_compose_gather
+    a = 0x100000
+    good = B.Sources([(a, 10), (a, 4)])
+    assert f(a, ctypes.byref(good.c), a, a, 0, 64, 1152, None, None) == B.OK  # no slots
+    assert f(a, None, a, a, 4, 64, 1152, None, None) == B.EINVAL
+    assert f(a, ctypes.byref(good.c), a, a, -1, 64, 1152, None, None) == B.EINVAL
+    assert f(a, ctypes.byref(good.c), a, a, 4, 0, 1152, None, None) == B.EINVAL
+    assert f(a, ctypes.byref(good.c), a, a, 4, 64, 1000, None, None) == B.EALIGN
+    assert f(a + 4, ctypes.byref(good.c), a, a, 4, 64, 1152, None, None) == B.EALIGN
+    assert f(None, ctypes.byref(good.c), a, a, 4, 64, 1152, None, None) == B.EINVAL
+    bad = B.Sources([(a + 8, 10)])
+    assert f(a, ctypes.byref(bad.c), a, a, 4, 64, 1152, None, None) == B.EALIGN
+    neg = B.Sources([(a, -1)])
+    assert f(a, ctypes.byref(neg.c), a, a, 4, 64, 1152, None, None) == B.EINVAL
+    empty = B.gpb_sources()
+    assert f(a, ctypes.byref(empty), a, a, 4, 64, 1152, None, None) == B.EINVAL
+    assert f(a, ctypes.byref(good.c), a, a, 4, 1 << 20, 4096, None, None) == B.ERANGE
+
+
+def test_staging_clear_argument_checks():
+    f = B.lib.gpb_staging_clear
+    assert f(0x100000, 0, None) == B.OK
+    assert f(0x100000, -16, None) == B.EINVAL
+    assert f(0x100008, 64, None) == B.EALIGN
+    assert f(0x100000, 40, None) == B.EALIGN
+    assert f(None, 64, None) == B.EINVAL
+
+
+_CODE_OF = {oracle.OK: {B.OK}, oracle.BAD_SHAPE: {B.EINVAL, B.EALIGN},
+            oracle.BAD_PAGE: {B.EPAGE}, oracle.CAPACITY: {B.ECAPACITY},
+            oracle.TOO_LARGE: {B.ERANGE}}
+
+
+def test_validation_agrees_with_oracle_on_random_batches(orc):
+    """Host validation of the library and the oracle accept and reject the
+    same batches, for the same reason."""
+    rng = np.random.default_rng(7)
+    n_bad = 0
+    for b in pins_random(rng, 400):
+        # break some batches: dummy page, duplicate, range, capacity
+        kind = rng.integers(0, 6)
+        pages = b.req_pages.copy()
+        cap = b.staging_cap_pages
+        if kind == 1 and len(pages):
+            pages[rng.integers(0, len(pages))] = 0
+        elif kind == 2 and len(pages) > 1:
+            pages[1] = pages[0]
+        elif kind == 3 and len(pages):
+            pages[-1] = b.n_pool_pages
+        elif kind == 4:
+            cap = max(1, cap - b.bs - 1)
+        want = orc.validate(b.bs, b.page_size, b.row_bytes, b.n_pool_pages,
+                            b.n_pool_entries, b.n_writers, cap, b.prefix_pages,
+                            b.cur_tokens, pages)
+        m = B.BatchMeta(b.bs, b.page_size, b.row_bytes, b.n_pool_pages, b.n_pool_entries,
+                        b.n_writers, cap, b.prefix_pages, b.cur_tokens, pages)
+        got = B.lib.gpb_plan_sizes(ctypes.byref(m.c), None, None, None)
+        assert got in _CODE_OF[want], (want, got)
+        n_bad += want != oracle.OK
+    assert n_bad > 50
+
+
+def pins_random(rng, n):
+    return [workloads.random_batch(rng) for _ in range(n)]

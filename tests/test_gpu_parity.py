@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, byte
+for byte, on the five workloads at full size and on random small batches.
+
+Every comparison is exact: the path moves integers and opaque bytes only.
+Inputs are seeded (workloads/); the oracle reads host copies of the very
+bytes the GPU reads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpb():
+    import gather_plan_build_amd as gpb
+    return gpb
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _runner(batch, pools, curs):
+    gpb = _gpb()
+    return gpb.ComposeRunner(gpb.BatchMeta.of(batch), pools, curs)
+
+
+def _host(t):
+    return t.cpu().numpy()
+
+
+def _check_plan(batch, r, orc):
+    want = oracle.plan_for(batch, orc)
+    for k in oracle.PLAN_FIELDS:
+        got = _host(r.plan.t[k])
+        assert np.array_equal(got, want[k]), "plan array %s differs" % k
+    return want
+
+
+def _oracle_layer(batch, want_plan, pool_np, cur_np, orc):
+    staging = np.full(batch.staging_rows_total * batch.row_bytes, 0xCD, np.uint8)
+    dense, bad = oracle.layer_for(batch, want_plan, pool_np.reshape(-1),
+                                  cur_np.reshape(-1, batch.row_bytes), staging, orc)
+    assert not bad
+    return dense, staging.reshape(-1, batch.row_bytes)
+
+
+def _check_layer(batch, r, layer, want_plan, pools_np, curs_np, orc, check_staging=True):
+    k = layer % len(pools_np)
+    dense, staging = _oracle_layer(batch, want_plan, pools_np[k], curs_np[k], orc)
+    got = _host(r.dense_of(layer))
+    assert got.shape == dense.shape
+    if not np.array_equal(got, dense):
+        bad_rows = np.nonzero((got != dense).any(axis=1))[0]
+        raise AssertionError("layer %d: %d dense rows differ, first %s"
+                             % (layer, len(bad_rows), bad_rows[:8].tolist()))
+    if check_staging:
+        assert np.array_equal(_host(r.staging_of(layer)), staging), \
+            "layer %d: staging differs" % layer
+
+
+def _status(r):
+    return int(r.status.item())
+
+
+def test_ragged_tails_stay_inside_their_ranges(orc):
+    """Pages whose chunk count is not a multiple of a workgroup's unit (656-
+    and 48-byte rows) and a scatter whose last workgroup runs past the last
+    row: every byte beyond the output range keeps its guard value."""
+    gpb = _gpb()
+    rng = np.random.default_rng(21)
+    for PS, RB in ((64, 656), (3, 48), (1, 16)):
+        n_pages, n_slots = 6, 5
+        pool_np = rng.integers(0, 256, (n_pages * PS, RB), dtype=np.uint8)
+        pool = torch.from_numpy(pool_np).cuda()
+        guard = 1 << 20
+        out = torch.full((n_slots * PS * RB + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        owner = torch.zeros(n_slots, dtype=torch.int32, device="cuda")
+        src = torch.tensor([5, 1, 4, 2, 3], dtype=torch.int32, device="cuda")
+        gpb.compose_gather(out, [(pool, n_pages)], owner, src, n_slots, PS, RB)
+        torch.cuda.synchronize()
+        h = _host(out)
+        assert (h[n_slots * PS * RB:] == 0x5A).all(), "gather wrote past its pages"
+        want = pool_np.reshape(n_pages, -1)[[5, 1, 4, 2, 3]].reshape(-1)
+        assert np.array_equal(h[:n_slots * PS * RB], want)
+
+        n_rows, n_stag = 7, 9
+        cur_np = rng.integers(0, 256, (n_rows, RB), dtype=np.uint8)
+        rows = np.array([8, 0, 2, 7, 1, 5, 6], np.int32)
+        stag = torch.full((n_stag * RB + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        gpb.current_row_scatter(stag, n_stag, torch.from_numpy(rows).cuda(),
+                                torch.from_numpy(cur_np).cuda(), n_rows, RB)
+        torch.cuda.synchronize()
+        h = _host(stag)
+        assert (h[n_stag * RB:] == 0x5A).all(), "scatter wrote past the staging"
+        want = np.full((n_stag, RB), 0x5A, np.uint8)
+        want[rows] = cur_np
+        assert np.array_equal(h[:n_stag * RB].reshape(n_stag, RB), want)
+        _say("guard ok", PS, RB)
+
+
+@pytest.mark.parametrize("name", workloads.CONFIGS)
+def test_plan_matches_oracle(orc, name):
+    b = workloads.make_batch(name)
+    _say("plan", name, "bs", b.bs, "slots", b.n_req_pages, "tokens", b.n_cur_tokens)
+    gpb = _gpb()
+    p = gpb.Plan(gpb.BatchMeta.of(b)).build()
+    torch.cuda.synchronize()
+    want = oracle.plan_for(b, orc)
+    for k in oracle.PLAN_FIELDS:
+        assert np.array_equal(_host(p.t[k]), want[k]), "plan array %s differs" % k
+
+
+def test_tiny_layer_byte_exact(orc):
+    b = workloads.make_batch("tiny")
+    pools, curs = workloads.make_values(b, device="cuda")
+    r = _runner(b, pools, curs)
+    r.run(1)
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    _check_layer(b, r, 0, want, [_host(p) for p in pools], [_host(c) for c in curs], orc)
+    assert _status(r) == 0
+
+
+@pytest.mark.parametrize("name", ["medium", "multi_source"])
+def test_single_layer_workloads(orc, name):
+    b = workloads.make_batch(name)
+    _say(name, "slots", b.n_req_pages, "tokens", b.n_cur_tokens)
+    pools, curs = workloads.make_values(b, device="cuda")
+    r = _runner(b, pools, curs)
+    r.run(b.n_layers)
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    _check_layer(b, r, 0, want, [_host(p) for p in pools], [_host(c) for c in curs], orc)
+    assert _status(r) == 0
+
+
+@pytest.mark.parametrize("name", ["traced", "opaque"])
+def test_multi_layer_workloads(orc, name):
+    """Full-size workloads: the first four layers one at a time (every pool
+    rotation), then the whole layer loop as bench.py runs it, checking the
+    last two layers (both parity halves)."""
+    b = workloads.make_batch(name)
+    _say(name, "layers", b.n_layers, "slots", b.n_req_pages, "tokens", b.n_cur_tokens)
+    pools, curs = workloads.make_values(b, device="cuda")
+    pools_np = [_host(p) for p in pools]
+    curs_np = [_host(c) for c in curs]
+    r = _runner(b, pools, curs)
+    r.begin_batch()
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    for layer in range(4):
+        r.layer(layer)
+        torch.cuda.synchronize()
+        _check_layer(b, r, layer, want, pools_np, curs_np, orc)
+        _say("  layer", layer, "ok")
+    r.run(b.n_layers)
+    torch.cuda.synchronize()
+    for layer in (b.n_layers - 2, b.n_layers - 1):
+        _check_layer(b, r, layer, want, pools_np, curs_np, orc)
+        _say("  layer", layer, "ok")
+    assert _status(r) == 0
+
+
+def _random_case(orc, b, layers=2):
+    pool_np, cur_np = pins.tagged_values(b)
+    pools = [torch.from_numpy(pool_np).cuda()]
+    curs = [torch.from_numpy(cur_np).cuda()]
+    r = _runner(b, pools, curs)
+    r.run(layers)
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    for layer in range(max(0, layers - 2), layers):
+        _check_layer(b, r, layer, want, [pool_np], [cur_np], orc)
+    assert _status(r) == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_small_batches(orc, seed):
+    """Edge-heavy random batches: empty and both-zero requests, current
+    lengths at page edges, page sizes 1..64, rows of 16..64 bytes, up to 3
+    pool entries and writers."""
+    for i, b in enumerate(pins.random_batches(60, seed=1000 + seed)):
+        _random_case(orc, b)
+    _say("seed", seed, "done")
+
+
+def test_many_requests_past_the_lds_stage(orc):
+    """bs = 1500 exceeds the requests staged in LDS (1024): the plan kernels
+    search the bases in global memory."""
+    rng = np.random.default_rng(3)
+    bs = 1500
+    P = rng.integers(0, 3, bs).astype(np.int32)
+    c = rng.choice([0, 1, 15, 16, 17, 40], bs).astype(np.int32)
+    PS = 16
+    n = int(P.sum() + ((c + PS - 1) // PS).sum())
+    pages = rng.choice(np.arange(1, n + 100), n, replace=False).astype(np.int32)
+    b = workloads.Batch("many", bs, PS, 32, n + 100, 2, 3,
+                        workloads.staging_cap_for(int(c.sum()), bs, PS), P, c, pages)
+    _random_case(orc, b)
+
+
+@pytest.mark.parametrize("ps,rb", [(1, 16), (2, 4096 + 16), (64, 656), (64, 1152), (3, 48)])
+def test_row_and_page_geometry(orc, ps, rb):
+    rng = np.random.default_rng(ps * 7 + rb)
+    for b in [workloads.random_batch(rng, page_size=ps, row_bytes=rb, max_pool=40)
+              for _ in range(6)]:
+        _random_case(orc, b)
+
+
+def test_empty_and_degenerate_batches(orc):
+    cases = [([], []), ([0, 0], [0, 0]), ([3, 2], [0, 0]), ([0, 0], [5, 64]),
+             ([1], [65])]
+    for P, c in cases:
+        P = np.array(P, np.int32)
+        c = np.array(c, np.int32)
+        n = int(P.sum() + ((c + 63) // 64).sum())
+        pages = np.arange(2, n + 2, dtype=np.int32)
+        b = workloads.Batch("edge", len(P), 64, 64, n + 3, 1, 1,
+                            workloads.staging_cap_for(int(c.sum()), len(P)), P, c, pages)
+        _random_case(orc, b)
+
+
+def test_sentinel_and_out_of_range_descriptors(orc):
+    """-1 descriptors zero-fill (page d63fbd4, commit "compose_v2"); a
+    descriptor outside the table or its arena is zero-filled and flagged."""
+    gpb = _gpb()
+    PS, RB = 4, 64
+    rng = np.random.default_rng(11)
+    pool_np = rng.integers(1, 256, (10 * PS, RB), dtype=np.uint8)
+    stag_np = rng.integers(1, 256, (3 * PS, RB), dtype=np.uint8)
+    pool = torch.from_numpy(pool_np).cuda()
+    stag = torch.from_numpy(stag_np).cuda()
+    owner = np.array([-1, 0, 1, 0, 2, 0, 1, -1], np.int32)
+    src = np.array([4, -1, 2, 9, 0, 10, 3, -1], np.int32)
+    dense = torch.full((len(owner) * PS, RB), 0x77, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gpb.compose_gather(dense, [(pool, 10), (stag, 3)], torch.from_numpy(owner).cuda(),
+                       torch.from_numpy(src).cuda(), len(owner), PS, RB, status)
+    torch.cuda.synchronize()
+    table = [pool_np.reshape(-1), stag_np.reshape(-1)]
+    want, bad = orc.compose_layer(table, np.zeros((0, RB), np.uint8), np.zeros(0, np.int32),
+                                  owner, src, PS, RB, np.zeros(RB, np.uint8))
+    assert bad
+    assert np.array_equal(_host(dense), want)
+    assert int(status.item()) == gpb.STATUS_BAD_DESCRIPTOR
+
+
+def test_out_of_range_staging_rows_are_skipped(orc):
+    gpb = _gpb()
+    RB = 32
+    rng = np.random.default_rng(12)
+    cur_np = rng.integers(1, 256, (5, RB), dtype=np.uint8)
+    rows = np.array([3, -1, 7, 8, 0], np.int32)        # 8 rows of staging: 8 is out
+    stag = torch.zeros((8, RB), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gpb.current_row_scatter(stag, 8, torch.from_numpy(rows).cuda(),
+                            torch.from_numpy(cur_np).cuda(), 5, RB, status)
+    torch.cuda.synchronize()
+    want = np.zeros((8, RB), np.uint8)
+    want[3], want[7], want[0] = cur_np[0], cur_np[2], cur_np[4]
+    assert np.array_equal(_host(stag), want)
+    assert int(status.item()) == gpb.STATUS_BAD_STAGING_ROW
+
+
+def test_staging_clear_zeroes_exactly(orc):
+    gpb = _gpb()
+    buf = torch.full((1 << 20,), 0xEE, dtype=torch.uint8, device="cuda")
+    gpb.staging_clear(buf[16:16 + 4096 * 37], 4096 * 37)
+    torch.cuda.synchronize()
+    h = _host(buf)
+    assert not h[16:16 + 4096 * 37].any()
+    assert (h[:16] == 0xEE).all() and (h[16 + 4096 * 37:] == 0xEE).all()
