@@ -24,6 +24,12 @@
 #ifndef GPB_SCATTER_CPT
 #define GPB_SCATTER_CPT 8
 #endif
+#ifndef GPB_LOAD_POLICY
+#define GPB_LOAD_POLICY 2   // cache-policy bits of the buffer loads (2 = nt)
+#endif
+#ifndef GPB_STORE_POLICY
+#define GPB_STORE_POLICY 2  // cache-policy bits of the buffer stores (2 = nt)
+#endif
 
 namespace gpb {
 namespace {
@@ -40,17 +46,16 @@ struct SrcTable {
 // branches around the memory instructions (branches around them would make
 // the compiler wait for each store before the next).
 constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw addressing
-constexpr int kNonTemporal = 2;         // each byte is touched once per layer
 constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every range we build
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
 }
 __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GPB_LOAD_POLICY);
 }
 __device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, GPB_STORE_POLICY);
 }
 
 // One workgroup per (slot, part).  The slot's descriptor is uniform across
@@ -236,12 +241,15 @@ extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
   hipStream_t st = as_stream(stream);
   const int32_t pc = static_cast<int32_t>(page_chunks);
   switch (pick_gather_cpt(page_chunks)) {
+    case 2: return launch_gather<2>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 3: return launch_gather<3>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     case 4: return launch_gather<4>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     case 6: return launch_gather<6>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     case 8: return launch_gather<8>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     case 9: return launch_gather<9>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     case 12: return launch_gather<12>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     case 16: return launch_gather<16>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
+    case 18: return launch_gather<18>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
     default: return GPB_EINVAL;
   }
 }
