@@ -10,10 +10,13 @@ Inputs are resident in HBM before timing starts.
 Prints one JSON line.  ``value`` is the whole job's algorithmic HBM
 throughput of the compose (bytes the method must move per layer -- read and
 write every dense page and every current row, plus descriptors -- times 78
-layers, over the measured step time).  Per-kernel durations come from HIP
-events recorded around every launch on the launch stream, inside the timed
-region.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the
-same layers on this host.
+layers, over the measured step time; the step also holds the plan build and
+staging clear, whose bytes are not counted).  The timed region holds the K
+steps and nothing else.  Per-kernel average durations come from regions of
+back-to-back launches of one kernel with the layer loop's arguments (HIP
+events on the launch stream around each region): events between kernels
+would add their own cache flushes to what they measure.  ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same layers on this host.
 """
 import argparse
 import hashlib
@@ -37,8 +40,13 @@ def _args():
                     choices=["traced", "opaque", "medium", "multi_source", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample (0 disables it)")
-    ap.add_argument("--no-kernel-events", action="store_true",
-                    help="time whole steps only (no per-launch events)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
+                    help="write profiles/ summaries from three rocprofv3 csv output "
+                         "directories (kernel trace + stats, FETCH_SIZE, WRITE_SIZE) "
+                         "and exit; runs on the host only")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="end with three torch copies of this size (counter "
+                         "calibration under rocprofv3)")
     return ap.parse_args()
 
 
@@ -116,8 +124,119 @@ def _cpu_model():
     return None
 
 
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    out = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix),
+                                 recursive=True)):
+        with open(path, newline="") as f:
+            out += list(csv.DictReader(f))
+    return out
+
+
+def _short(name):
+    for key in ("k_compose_gather", "k_row_scatter", "k_fill_zero", "k_plan_scan_fill",
+                "k_plan_slots", "k_plan_tokens", "copyBuffer"):
+        if key in name:
+            return key
+    return name[:60]
+
+
+PROFILE_COMMANDS = {
+    "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py "
+             "--steps 3 --warmup 1 --cpu-seconds 0",
+    "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv "
+             "-d $REPO/gpurun_out/prof_fetch -o fetch -- python3 $REPO/bench.py "
+             "--steps 1 --warmup 0 --cpu-seconds 0 --calibration-copy-mib 1024",
+    "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv "
+             "-d $REPO/gpurun_out/prof_write -o write -- python3 $REPO/bench.py "
+             "--steps 1 --warmup 0 --cpu-seconds 0 --calibration-copy-mib 1024",
+    "summary": "python3 bench.py --summarize-profiles gpurun_out/prof_trace "
+               "gpurun_out/prof_fetch gpurun_out/prof_write",
+}
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
+    """profiles/<kernel>_<workload>_kernels.txt (rocprofv3 kernel statistics)
+    and profiles/compose_gather_<workload>_counters.{json,txt} (HBM bytes per
+    gather launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
+    counter reads for a plain 1 GiB copy)."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    lines = ["# rocprofv3 kernel statistics, %s workload (bench.py)" % workload,
+             "# command: " + PROFILE_COMMANDS["trace"],
+             "# source digest of gather_plan_build_amd/csrc: " + _source_digest(),
+             "%-22s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
+                                              "max_ns", "pct")]
+    for r in stats:
+        lines.append("%-22s %7s %12.0f %12.0f %12.0f %8.2f" % (
+            _short(r["Name"]), r["Calls"], float(r["AverageNs"]), float(r["MinNs"]),
+            float(r["MaxNs"]), float(r["Percentage"])))
+    with open(os.path.join(prof, "compose_%s_kernels.txt" % workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(directory, counter):
+        acc = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return acc
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    # the calibration copies are the largest copyBuffer dispatches (1 GiB each;
+    # the other copies are the 64 MiB input-generation chunks)
+    copy_kib = 1024 * 1024.0
+    f_copy, w_copy = max(fetch["copyBuffer"]), max(write["copyBuffer"])
+    f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
+    rec = {"workload": workload, "source_digest": _source_digest(),
+           "commands": PROFILE_COMMANDS,
+           "calibration": {"copy_bytes": int(copy_kib * 1024), "fetch_kib": f_copy,
+                           "write_kib": w_copy, "fetch_scale": f_scale,
+                           "write_scale": w_scale},
+           "kernels": {}}
+    for k in ("k_compose_gather", "k_row_scatter"):
+        if k in fetch and k in write:
+            fk = sum(fetch[k]) / len(fetch[k])
+            wk = sum(write[k]) / len(write[k])
+            rec["kernels"][k] = {
+                "dispatches": len(fetch[k]), "fetch_kib_raw": round(fk, 1),
+                "write_kib_raw": round(wk, 1),
+                "read_bytes": round(1024 * fk * f_scale),
+                "write_bytes": round(1024 * wk * w_scale),
+                "hbm_bytes_per_launch": round(1024 * (fk * f_scale + wk * w_scale))}
+    if "k_compose_gather" in rec["kernels"]:
+        rec["hbm_bytes_per_launch"] = rec["kernels"]["k_compose_gather"]["hbm_bytes_per_launch"]
+    with open(os.path.join(prof, "compose_gather_%s_counters.json" % workload), "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1, sort_keys=True))
+    return rec
+
+
+def _timed(stream, fn, reps):
+    """Average ms of ``fn`` over ``reps`` back-to-back calls, HIP events on
+    the launch stream around the whole region."""
+    import torch
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / reps
+
+
 def main():
     a = _args()
+    if a.summarize_profiles:
+        summarize_profiles(*a.summarize_profiles, workload=a.workload)
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU only: the compose path here has no "
               "multi-GPU transport (the pointer table would hold peer addresses); "
@@ -134,38 +253,13 @@ def main():
     L = batch.n_layers
     stream = torch.cuda.current_stream()
 
-    def step(ev):
-        if ev is None:
-            runner.run(L, stream)
-            return
-        ev["plan"][0].record(stream)
-        runner.begin_batch(stream)
-        ev["plan"][1].record(stream)
-        marks = ev["marks"]
-        for layer in range(L):
-            runner.scatter(layer, stream)
-            marks[2 * layer].record(stream)
-            runner.gather(layer, stream)
-            marks[2 * layer + 1].record(stream)
-
-    def new_events():
-        E = torch.cuda.Event
-        return {"plan": [E(enable_timing=True), E(enable_timing=True)],
-                "marks": [E(enable_timing=True) for _ in range(2 * L)]}
+    def step():
+        runner.run(L, stream)
 
     for _ in range(a.warmup):
-        step(None)
-    torch.cuda.synchronize()
-
-    evs = [None if a.no_kernel_events else new_events() for _ in range(a.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(a.steps):
-        step(evs[s])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / a.steps
+        step()
+    # the timed region: K whole steps, nothing else on the stream
+    ms_per_step = _timed(stream, step, a.steps)
     assert int(runner.status.item()) == 0, "a kernel flagged a bad descriptor or row"
 
     layer_bytes = runner.algorithmic_bytes_per_layer()
@@ -182,34 +276,33 @@ def main():
                       "global_batch": batch.bs, "seq_len": None,
                       "parallelism": "single GPU",
                       "algorithmic_bytes_per_layer": layer_bytes}}
-    if not a.no_kernel_events:
-        gather_ms, scatter_ms, plan_ms = [], [], []
-        for ev in evs:
-            m = ev["marks"]
-            plan_ms.append(ev["plan"][0].elapsed_time(ev["plan"][1]))
-            scatter_ms.append(ev["plan"][1].elapsed_time(m[0]))
-            for layer in range(L):
-                if layer:
-                    scatter_ms.append(m[2 * layer - 1].elapsed_time(m[2 * layer]))
-                gather_ms.append(m[2 * layer].elapsed_time(m[2 * layer + 1]))
-        g_us = 1e3 * sum(gather_ms) / len(gather_ms)
-        s_us = 1e3 * sum(scatter_ms) / len(scatter_ms)
-        compose_us = g_us + s_us
-        g_bytes = runner.gather_bytes()
-        achieved = g_bytes / (g_us * 1e-6) / 1e9
-        traffic = _traffic(a.workload, g_bytes)
-        out["us_per_layer"] = round(compose_us, 2)
-        out["compose_gbs"] = round(layer_bytes / (compose_us * 1e-6) / 1e9, 1)
-        out["pct_of_peak"] = round(100.0 * out["compose_gbs"] / HBM_PEAK_GBS, 2)
-        out["kernels_us"] = {"compose_gather": round(g_us, 2),
-                             "current_row_scatter": round(s_us, 2),
-                             "plan_build_and_staging_clear": round(
-                                 1e3 * sum(plan_ms) / len(plan_ms), 2)}
-        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": traffic,
-                           "kernel": "compose_gather", "bytes_per_launch": g_bytes}
+    # per-kernel averages: each kernel alone, launched back to back with the
+    # layer loop's arguments, K*L launches per region
+    reps = a.steps
+    g_ms = _timed(stream, lambda: [runner.gather(l, stream) for l in range(L)], reps) / L
+    s_ms = _timed(stream, lambda: [runner.scatter(l, stream) for l in range(L)], reps) / L
+    p_ms = _timed(stream, lambda: runner.begin_batch(stream), reps)
+    g_us, s_us = g_ms * 1e3, s_ms * 1e3
+    g_bytes = runner.gather_bytes()
+    achieved = g_bytes / (g_us * 1e-6) / 1e9
+    out["us_per_layer"] = round((ms_per_step - p_ms) * 1e3 / L, 2)
+    out["pct_of_peak"] = round(100.0 * layer_bytes / (out["us_per_layer"] * 1e-6) / 1e9
+                               / HBM_PEAK_GBS, 2)
+    out["kernels_us"] = {"compose_gather": round(g_us, 2),
+                         "current_row_scatter": round(s_us, 2),
+                         "plan_build_and_staging_clear": round(p_ms * 1e3, 2)}
+    out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
+                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(achieved / HBM_PEAK_GBS, 4),
+                       "traffic": _traffic(a.workload, g_bytes),
+                       "kernel": "compose_gather", "bytes_per_launch": g_bytes}
+    if a.calibration_copy_mib:
+        n = a.calibration_copy_mib << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
     if a.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(batch, pools, curs, a.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -9,26 +9,43 @@
 // d63fbd4, commit "compose_v2": -1 descriptors zero-fill.  Page 0d87bc5,
 // commit "fp8 index_copy_ -> uint8 views": rows are opaque bytes.
 //
-// Both per-layer kernels are HBM-bound copies.  Every lane moves 16-byte
-// chunks (buffer_load_dwordx4 / buffer_store_dwordx4), issues all of its
-// loads before its first store so several are in flight, and marks the
-// traffic non-temporal: each byte is read once and written once per layer.
+// Both per-layer kernels are HBM-bound copies with no arithmetic to speak of,
+// so the design is about the memory system only:
+//   - every lane moves 16-byte chunks (buffer_load_dwordx4 /
+//     buffer_store_dwordx4), a wave64 moves one contiguous KiB per
+//     instruction;
+//   - the work is cut into many small units (one wave, one KiB per unit by
+//     default), walked in address order: on MI355X this measured faster than
+//     fewer, larger units (more chunks in flight per lane, 256-lane
+//     workgroups), than part-major orders and than XCD-blocked orders;
+//   - loads and stores are non-temporal: each byte is read once and written
+//     once per layer;
+//   - raw buffer resources bound every access, so ragged tails, -1 sentinels
+//     and bad rows cost no branches.
+// The unit shape and cache-policy bits can be overridden at build time
+// (-DGPB_GATHER_CPT=..., etc.) for tuning; the defaults are the measured best.
 #include <algorithm>
 #include <cstdio>
 
 #include "gpb_common.h"
 
+#ifndef GPB_GATHER_BLOCK
+#define GPB_GATHER_BLOCK 64    // lanes per gather workgroup (one wave64)
+#endif
 #ifndef GPB_GATHER_CPT
-#define GPB_GATHER_CPT 0   // 0: chosen per shape at launch
+#define GPB_GATHER_CPT 1       // 16-byte chunks per lane per unit
+#endif
+#ifndef GPB_SCATTER_BLOCK
+#define GPB_SCATTER_BLOCK 64   // lanes per scatter workgroup
 #endif
 #ifndef GPB_SCATTER_CPT
-#define GPB_SCATTER_CPT 8
+#define GPB_SCATTER_CPT 1      // 16-byte chunks per lane
 #endif
 #ifndef GPB_LOAD_POLICY
-#define GPB_LOAD_POLICY 2   // cache-policy bits of the buffer loads (2 = nt)
+#define GPB_LOAD_POLICY 2      // cache-policy bits of the buffer loads (nt)
 #endif
 #ifndef GPB_STORE_POLICY
-#define GPB_STORE_POLICY 2  // cache-policy bits of the buffer stores (2 = nt)
+#define GPB_STORE_POLICY 2     // cache-policy bits of the buffer stores (nt)
 #endif
 
 namespace gpb {
@@ -45,7 +62,7 @@ struct SrcTable {
 // outside it is dropped, so ragged tails, -1 sentinels and bad rows need no
 // branches around the memory instructions (branches around them would make
 // the compiler wait for each store before the next).
-constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw addressing
+constexpr int kRsrcWord3 = 0x00020000;         // 32-bit data format, raw addressing
 constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every range we build
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
@@ -58,13 +75,13 @@ __device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, GPB_STORE_POLICY);
 }
 
-// One workgroup per (slot, part).  The slot's descriptor is uniform across
-// the workgroup: owner/src are scalar loads and both buffer resources live in
-// scalar registers.  Lane l moves chunks l, l + 256, ... of the part, so each
-// wave's access is one contiguous 1 KiB run.  An invalid or -1 descriptor
-// gets a source range of 0 bytes: every load returns zeros.
-template <int CPT>
-__global__ __launch_bounds__(kBlock) void k_compose_gather(
+// One workgroup per unit of a slot's page, units of a page consecutive.  The
+// slot's descriptor is uniform across the workgroup: owner/src are scalar
+// loads and both buffer resources live in scalar registers.  Lane l moves
+// chunks l, l + B, ... of the unit.  An invalid or -1 descriptor gets a
+// source range of 0 bytes: every load returns zeros.
+template <int B, int CPT>
+__global__ __launch_bounds__(B) void k_compose_gather(
     uint8_t *__restrict__ dense, SrcTable tbl, const int32_t *__restrict__ owner,
     const int32_t *__restrict__ src, int32_t page_bytes, int32_t parts,
     int32_t *status) {
@@ -76,33 +93,34 @@ __global__ __launch_bounds__(kBlock) void k_compose_gather(
   const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
   const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
   const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
-  const __amdgpu_buffer_rsrc_t rd = rsrc(dense + static_cast<int64_t>(slot) * page_bytes, page_bytes);
-  const uint32_t first = (static_cast<uint32_t>(part) * (kBlock * CPT) + threadIdx.x) * 16u;
+  const __amdgpu_buffer_rsrc_t rd =
+      rsrc(dense + static_cast<int64_t>(slot) * page_bytes, page_bytes);
+  const uint32_t first = (static_cast<uint32_t>(part) * (B * CPT) + threadIdx.x) * 16u;
   u32x4 v[CPT];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) v[k] = ld16(rs, first + k * (kBlock * 16));
+  for (int k = 0; k < CPT; ++k) v[k] = ld16(rs, first + k * (B * 16));
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) st16(v[k], rd, first + k * (kBlock * 16));
+  for (int k = 0; k < CPT; ++k) st16(v[k], rd, first + k * (B * 16));
   if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
     atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
 }
 
 // Flat over (row, chunk) of the current rows: lane g of the grid handles
-// chunks g, g + 256, ... of its workgroup's range; the (row, offset) pair
-// advances by the precomputed (256 div row_chunks, 256 mod row_chunks), so a
-// lane divides once.  Consecutive lanes read consecutive source chunks; the
+// chunks g, g + B, ... of its workgroup's range; the (row, offset) pair
+// advances by the precomputed (B div row_chunks, B mod row_chunks), so a lane
+// divides once.  Consecutive lanes read consecutive source chunks; the
 // destination row of each chunk comes from staging_rows.  Chunks past the
 // last row read zeros and their stores go to kDropOffset (dropped), as do
 // rows whose staging row is out of range.
-template <int CPT>
-__global__ __launch_bounds__(kBlock) void k_row_scatter(
+template <int B, int CPT>
+__global__ __launch_bounds__(B) void k_row_scatter(
     uint8_t *__restrict__ staging, int32_t staging_bytes, int32_t n_staging_rows,
     const int32_t *__restrict__ rows, const uint8_t *__restrict__ cur,
     int32_t n_rows, int32_t row_chunks, int32_t step_rows, int32_t step_off,
     int32_t *status) {
   const __amdgpu_buffer_rsrc_t rs = rsrc(cur, n_rows * row_chunks * 16);
   const __amdgpu_buffer_rsrc_t rd = rsrc(staging, staging_bytes);
-  const int g = blockIdx.x * (kBlock * CPT) + threadIdx.x;
+  const int g = blockIdx.x * (B * CPT) + threadIdx.x;
   int row = g / row_chunks;
   int off = g - row * row_chunks;
   u32x4 v[CPT];
@@ -128,41 +146,16 @@ __global__ __launch_bounds__(kBlock) void k_row_scatter(
   if (bad && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
 }
 
+// Flat: lane g of the grid zeroes chunks g, g + 256, g + 512, g + 768 of its
+// workgroup's 1024-chunk range.
 __global__ __launch_bounds__(kBlock) void k_fill_zero(u32x4 *__restrict__ p,
                                                       int64_t n_chunks) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-       i < n_chunks; i += stride)
-    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, p + i);
-}
-
-// Chunks per lane for a page of `page_chunks` chunks: the candidate that
-// wastes the fewest lane slots in the last part, then the larger unit.
-int pick_gather_cpt(int64_t page_chunks) {
-  if (GPB_GATHER_CPT > 0) return GPB_GATHER_CPT;
-  static const int cand[] = {16, 12, 9, 8, 6, 4};
-  int best = cand[0];
-  int64_t best_waste = INT64_MAX;
-  for (int c : cand) {
-    const int64_t unit = static_cast<int64_t>(kBlock) * c;
-    const int64_t waste = ceil_div64(page_chunks, unit) * unit - page_chunks;
-    if (waste < best_waste) {
-      best = c;
-      best_waste = waste;
-    }
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * 4) + threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = first + k * kBlock;
+    if (i < n_chunks) __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, p + i);
   }
-  return best;
-}
-
-template <int CPT>
-int launch_gather(uint8_t *dense, const SrcTable &t, const int32_t *owner,
-                  const int32_t *src, int32_t n_slots, int32_t page_chunks,
-                  int32_t *status, hipStream_t st) {
-  const int64_t parts = ceil_div64(page_chunks, static_cast<int64_t>(kBlock) * CPT);
-  const int64_t grid = parts * n_slots;
-  if (grid > INT32_MAX) return GPB_ERANGE;
-  return launch(k_compose_gather<CPT>, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
-                st, dense, t, owner, src, page_chunks * 16, parts, status);
 }
 
 }  // namespace
@@ -175,7 +168,8 @@ extern "C" int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream) {
   if (!d_ptr) return GPB_EINVAL;
   if (n_bytes % 16 != 0 || !aligned(d_ptr, 16)) return GPB_EALIGN;
   const int64_t chunks = n_bytes / 16;
-  const int64_t grid = std::min<int64_t>(ceil_div64(chunks, kBlock * 4), 4096);
+  const int64_t grid = ceil_div64(chunks, kBlock * 4);
+  if (grid > INT32_MAX) return GPB_ERANGE;
   return launch(k_fill_zero, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
                 as_stream(stream), static_cast<u32x4 *>(d_ptr), chunks);
 }
@@ -186,7 +180,7 @@ extern "C" int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
                                        int32_t row_bytes, int32_t *d_status,
                                        void *stream) {
   using namespace gpb;
-  constexpr int CPT = GPB_SCATTER_CPT;
+  constexpr int B = GPB_SCATTER_BLOCK, CPT = GPB_SCATTER_CPT;
   if (n_rows < 0 || n_staging_rows < 0 || row_bytes < 1) return GPB_EINVAL;
   if (n_staging_rows > INT32_MAX) return GPB_ERANGE;
   if (row_bytes % 16 != 0) return GPB_EALIGN;
@@ -201,11 +195,11 @@ extern "C" int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
   const int64_t staging_bytes = n_staging_rows * row_bytes;
   if (cur_bytes > INT32_MAX || staging_bytes > INT32_MAX) return GPB_ERANGE;
   const int64_t total = static_cast<int64_t>(n_rows) * row_chunks;
-  const int64_t grid = ceil_div64(total, static_cast<int64_t>(kBlock) * CPT);
-  return launch(k_row_scatter<CPT>, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
+  const int64_t grid = ceil_div64(total, static_cast<int64_t>(B) * CPT);
+  return launch(k_row_scatter<B, CPT>, dim3(static_cast<uint32_t>(grid)), dim3(B),
                 as_stream(stream), d_staging, staging_bytes, n_staging_rows,
-                d_staging_rows, d_cur_rows, n_rows, row_chunks, kBlock / row_chunks,
-                kBlock % row_chunks, d_status);
+                d_staging_rows, d_cur_rows, n_rows, row_chunks, B / row_chunks,
+                B % row_chunks, d_status);
 }
 
 extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
@@ -214,13 +208,14 @@ extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
                                   int32_t row_bytes, int32_t *d_status,
                                   void *stream) {
   using namespace gpb;
+  constexpr int B = GPB_GATHER_BLOCK, CPT = GPB_GATHER_CPT;
   if (!table || n_slots < 0 || page_rows < 1 || row_bytes < 1) return GPB_EINVAL;
   if (table->n < 1 || table->n > GPB_MAX_SOURCES) return GPB_EINVAL;
   if (row_bytes % 16 != 0) return GPB_EALIGN;
   if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
-  const int64_t page_chunks = static_cast<int64_t>(page_rows) * (row_bytes / 16);
-  // a page is one buffer range: 32-bit byte count
-  if (page_chunks * 16 > INT32_MAX - 16 * kBlock * 16) return GPB_ERANGE;
+  const int64_t page_bytes = static_cast<int64_t>(page_rows) * row_bytes;
+  // a page is one buffer range: 32-bit byte count, with room for the last unit
+  if (page_bytes > INT32_MAX - (1 << 20)) return GPB_ERANGE;
   SrcTable t;
   t.n = table->n;
   for (int e = 0; e < GPB_MAX_SOURCES; ++e) {
@@ -237,21 +232,11 @@ extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
   if (n_slots == 0) return GPB_OK;
   if (!d_dense || !d_owner || !d_src) return GPB_EINVAL;
   if (!aligned(d_dense, 16) || !aligned(d_owner, 4) || !aligned(d_src, 4)) return GPB_EALIGN;
-  uint8_t *dense = static_cast<uint8_t *>(d_dense);
-  hipStream_t st = as_stream(stream);
-  const int32_t pc = static_cast<int32_t>(page_chunks);
-  switch (pick_gather_cpt(page_chunks)) {
-    case 2: return launch_gather<2>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 3: return launch_gather<3>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 4: return launch_gather<4>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 6: return launch_gather<6>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 8: return launch_gather<8>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 9: return launch_gather<9>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 12: return launch_gather<12>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 16: return launch_gather<16>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    case 18: return launch_gather<18>(dense, t, d_owner, d_src, n_slots, pc, d_status, st);
-    default: return GPB_EINVAL;
-  }
+  const int64_t parts = ceil_div64(page_bytes / 16, static_cast<int64_t>(B) * CPT);
+  const int64_t grid = parts * n_slots;
+  if (grid > INT32_MAX) return GPB_ERANGE;
+  return launch(k_compose_gather<B, CPT>, dim3(static_cast<uint32_t>(grid)), dim3(B),
+                as_stream(stream), d_dense, t, d_owner, d_src, page_bytes, parts, d_status);
 }
 
 namespace gpb {
