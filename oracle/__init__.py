@@ -29,10 +29,13 @@ Parity status per function (pins in tests/test_oracle_pins.py):
   staging_page_inverse, owner, src, writer, staging_rows, mixed_locs),
   compose_layer, closed_form.dense -- pinned (brute force on tagged rows,
   closed form, library special cases, hand-derived worked example);
-  q_lens, kv_lens, q_starts, k_bases, current_bases, q_bases -- the pages
-  give only their names; pinned to the stated definitions through the dense
-  and staging geometry they must agree with; "parity unpinned" as far as
-  the pages themselves go.
+  token_req -- pinned to numpy repeat (the repeat_interleave the pages used);
+  prefix_slots, current_slots, pool_locs, gather_slots, fill -- pinned by
+  brute force on tagged rows and against the full gather;
+  q_lens, kv_lens, q_starts, k_bases, current_bases, q_bases, topk_offsets,
+  segments -- the pages give only their names; pinned to the stated
+  definitions through the dense and staging geometry they must agree with;
+  "parity unpinned" as far as the pages themselves go.
 """
 import ctypes
 import os
@@ -50,7 +53,11 @@ OK, BAD_SHAPE, BAD_PAGE, CAPACITY, TOO_LARGE = 0, 1, 2, 3, 4
 PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
                "q_starts", "k_bases", "q_bases", "current_bases", "slot_pages",
                "owner", "src", "page_inverse", "staging_page_inverse", "writer",
-               "staging_rows", "mixed_locs")
+               "staging_rows", "mixed_locs", "token_req", "topk_offsets", "segments",
+               "prefix_slots", "current_slots", "pool_locs")
+# the arrays gpbo_plan writes; the next three come from gpbo_token_expansions,
+# the last three from gpbo_prefetch_lists
+_PLAN_CORE = PLAN_FIELDS[:-6]
 
 
 def _i32(a):
@@ -72,6 +79,10 @@ class Oracle:
         lib.gpbo_plan.restype = ctypes.c_int
         lib.gpbo_layer.restype = ctypes.c_int
         lib.gpbo_counts.restype = None
+        lib.gpbo_token_expansions.restype = None
+        lib.gpbo_prefetch_lists.restype = None
+        lib.gpbo_gather_slots.restype = ctypes.c_int
+        lib.gpbo_fill.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
@@ -119,7 +130,9 @@ class Oracle:
                  "q_bases": bs, "current_bases": bs, "slot_pages": S,
                  "owner": S, "src": S, "page_inverse": n_pool_pages,
                  "staging_page_inverse": n_pool_pages, "writer": NCP,
-                 "staging_rows": T, "mixed_locs": T}
+                 "staging_rows": T, "mixed_locs": T, "token_req": T,
+                 "topk_offsets": T, "segments": 4 * bs, "prefix_slots": S - NCP,
+                 "current_slots": NCP, "pool_locs": T}
         # -7 marks entries the oracle never wrote; each array carries a guard
         # tail as long as itself that must stay untouched
         out = {k: np.full(2 * sizes[k] + 64, -7, dtype=np.int32) for k in PLAN_FIELDS}
@@ -129,9 +142,17 @@ class Oracle:
         rc = self.lib.gpbo_plan(bs, page_size, row_bytes, n_pool_pages,
                                 n_pool_entries, n_writers, staging_cap_pages,
                                 pP, pc, pg,
-                                *[out[k].ctypes.data_as(_I32P) for k in PLAN_FIELDS])
+                                *[out[k].ctypes.data_as(_I32P) for k in _PLAN_CORE])
         if rc != OK:
             raise ValueError(rc)
+        self.lib.gpbo_token_expansions(bs, page_size, pP, pc,
+                                       out["token_req"].ctypes.data_as(_I32P),
+                                       out["topk_offsets"].ctypes.data_as(_I32P),
+                                       out["segments"].ctypes.data_as(_I32P))
+        self.lib.gpbo_prefetch_lists(bs, page_size, pP, pc, pg,
+                                     out["prefix_slots"].ctypes.data_as(_I32P),
+                                     out["current_slots"].ctypes.data_as(_I32P),
+                                     out["pool_locs"].ctypes.data_as(_I32P))
         for k in PLAN_FIELDS:
             assert np.all(out[k][sizes[k]:] == -7), "oracle wrote past " + k
         return {k: out[k][:sizes[k]].copy() for k in PLAN_FIELDS}
@@ -165,6 +186,37 @@ class Oracle:
                                   n_rows, psr, pow_, psc, n_slots, page_size,
                                   RB, _p(dense))
         return dense, bool(bad)
+
+
+    def gather_slots(self, table, slots, owner, src, page_size, row_bytes, dense):
+        """O14: gather the listed slots into ``dense`` (uint8 [S*PS, RB]),
+        leaving the others.  Returns the out-of-range flag."""
+        RB = int(row_bytes)
+        assert dense.dtype == np.uint8 and dense.flags.c_contiguous
+        n_tab = max(len(table), 1)
+        ptrs = (ctypes.c_void_p * n_tab)(*[t.ctypes.data for t in table])
+        pages = (ctypes.c_int64 * n_tab)(*[t.size // (page_size * RB) for t in table])
+        sl, psl = _i32(slots)
+        ow, pow_ = _i32(owner)
+        sc, psc = _i32(src)
+        assert len(sl) == 0 or (sl.min() >= 0 and sl.max() < len(ow)
+                                and dense.size >= len(ow) * page_size * RB)
+        return bool(self.lib.gpbo_gather_slots(ptrs, pages, len(table), psl, len(sl),
+                                               pow_, psc, page_size, RB, _p(dense)))
+
+    def fill(self, staging, staging_rows, pool, pool_locs, cur, row_bytes):
+        """O15: each current row to its staging row and its pool row (uint8
+        arrays updated in place).  Returns the out-of-range flag."""
+        RB = int(row_bytes)
+        for a in (staging, pool):
+            assert a.dtype == np.uint8 and a.flags.c_contiguous and a.size % RB == 0
+        cur = np.ascontiguousarray(cur, dtype=np.uint8)
+        sr, psr = _i32(staging_rows)
+        pl_, ppl = _i32(pool_locs)
+        assert len(sr) == len(pl_) and cur.size >= len(sr) * RB
+        return bool(self.lib.gpbo_fill(_p(staging), ctypes.c_int64(staging.size // RB), psr,
+                                       _p(pool), ctypes.c_int64(pool.size // RB), ppl,
+                                       _p(cur), len(sr), RB))
 
 
 def pointer_table(pool, staging, n_pool_entries, n_writers, staging_cap_pages,

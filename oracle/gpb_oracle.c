@@ -246,3 +246,111 @@ int gpbo_layer(const uint8_t *const *table, const int64_t *table_pages,
   }
   return bad;
 }
+
+/*
+ * O12: per-token ragged expansions, built once per batch ([CG]: the
+ * O(total-q-tokens) top-k offset list and the segment records of the ragged
+ * index plan; page 0d87bc5, commit "flattened request row ids": row ids that
+ * the pages built with repeat_interleave over per-request lengths).  For every
+ * current token t (token-packed, request order):
+ *   token_req[t]     the request it belongs to;
+ *   topk_offsets[t]  the dense row where that request's KV starts, so a
+ *                    request-relative KV position (a top-k index) plus the
+ *                    offset is a row of the composed dense buffer.
+ * For every request r one segment record of four int32:
+ *   (first token, tokens, first dense row, KV rows = PS * P_r + c_r).
+ */
+void gpbo_token_expansions(int32_t bs, int32_t page_size,
+                           const int32_t *prefix_pages, const int32_t *cur_tokens,
+                           int32_t *token_req, int32_t *topk_offsets,
+                           int32_t *segments) {
+  int32_t token = 0, dense_row = 0;
+  for (int32_t r = 0; r < bs; r++) {
+    int32_t pages = prefix_pages[r] + (int32_t)ceil_div(cur_tokens[r], page_size);
+    for (int32_t j = 0; j < cur_tokens[r]; j++) {
+      token_req[token + j] = r;
+      topk_offsets[token + j] = dense_row;
+    }
+    segments[4 * r + 0] = token;
+    segments[4 * r + 1] = cur_tokens[r];
+    segments[4 * r + 2] = dense_row;
+    segments[4 * r + 3] = page_size * prefix_pages[r] + cur_tokens[r];
+    token += cur_tokens[r];
+    dense_row += page_size * pages;
+  }
+}
+
+/*
+ * O13: lists for the layer-ahead prefetch (page 0d87bc5, commit "prefetch
+ * staging exchange": the prefetcher fills the dense buffer's prefix a layer
+ * ahead; the consume step fills the current rows into staging and gathers
+ * ALL current pages from the staging).  From the batch metadata alone:
+ *   prefix_slots[u]   dense slot of the u-th prefix page of the batch
+ *                     (requests in order, pages in order)   [S - NCP]
+ *   current_slots[i]  dense slot of current page i           [NCP]
+ *   pool_locs[t]      pool row of current token t: its page is the request's
+ *                     listed current page j / PS, row j mod PS   [T]
+ */
+void gpbo_prefetch_lists(int32_t bs, int32_t page_size,
+                         const int32_t *prefix_pages, const int32_t *cur_tokens,
+                         const int32_t *req_pages, int32_t *prefix_slots,
+                         int32_t *current_slots, int32_t *pool_locs) {
+  int32_t slot = 0, u = 0, i = 0, token = 0;
+  for (int32_t r = 0; r < bs; r++) {
+    for (int32_t k = 0; k < prefix_pages[r]; k++) prefix_slots[u++] = slot++;
+    int32_t first_cur = slot;
+    int32_t pages = (int32_t)ceil_div(cur_tokens[r], page_size);
+    for (int32_t k = 0; k < pages; k++) current_slots[i++] = slot++;
+    for (int32_t j = 0; j < cur_tokens[r]; j++)
+      pool_locs[token++] = req_pages[first_cur + j / page_size] * page_size + j % page_size;
+  }
+}
+
+/*
+ * O14: gather only the listed dense slots (the prefetch half or the current
+ * half of a layer's gather); every other slot of `dense` is left as it is.
+ * Same descriptor rules as O10.  Returns 1 if a descriptor was out of range.
+ */
+int gpbo_gather_slots(const uint8_t *const *table, const int64_t *table_pages,
+                      int32_t n_src, const int32_t *slots, int32_t n,
+                      const int32_t *owner, const int32_t *src, int32_t page_size,
+                      int32_t row_bytes, uint8_t *dense) {
+  int bad = 0;
+  const int64_t page_bytes = (int64_t)page_size * row_bytes;
+  for (int32_t k = 0; k < n; k++) {
+    int32_t s = slots[k];
+    uint8_t *out = dense + (int64_t)s * page_bytes;
+    int32_t e = owner[s], p = src[s];
+    if (e < 0 || p < 0) { memset(out, 0, (size_t)page_bytes); continue; }
+    if (e >= n_src || p >= table_pages[e]) {
+      bad = 1;
+      memset(out, 0, (size_t)page_bytes);
+      continue;
+    }
+    memcpy(out, table[e] + (int64_t)p * page_bytes, (size_t)page_bytes);
+  }
+  return bad;
+}
+
+/*
+ * O15: the fused current fill: every current row goes to its staging row
+ * (as the scatter) and to its pool row (its KV-cache location), whole rows
+ * of bytes.  Rows whose destination is out of range are skipped there and
+ * reported (returns 1).  Nothing is zeroed here.
+ */
+int gpbo_fill(uint8_t *staging, int64_t n_staging_rows, const int32_t *staging_rows,
+              uint8_t *pool, int64_t n_pool_rows, const int32_t *pool_locs,
+              const uint8_t *cur, int32_t n_rows, int32_t row_bytes) {
+  int bad = 0;
+  const int64_t RB = row_bytes;
+  for (int32_t t = 0; t < n_rows; t++) {
+    const uint8_t *row = cur + (int64_t)t * RB;
+    int64_t d = staging_rows[t];
+    if (d < 0 || d >= n_staging_rows) bad = 1;
+    else memcpy(staging + d * RB, row, (size_t)RB);
+    int64_t q = pool_locs[t];
+    if (q < 0 || q >= n_pool_rows) bad = 1;
+    else memcpy(pool + q * RB, row, (size_t)RB);
+  }
+  return bad;
+}

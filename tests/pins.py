@@ -152,6 +152,31 @@ def pin_plan_geometry(batch, pl, dense, staging):
     ml = pl["mixed_locs"]
     assert np.all(kind[ml] == KIND_CUR) and np.array_equal(idx[ml], np.arange(T))
 
+    # per-token expansions: request row ids are numpy's repeat of the request
+    # index over the token counts; the top-k offset of a token is the first
+    # dense row of its request, so offset + KV position lands on the row that
+    # holds that position (prefix row x, or the token itself)
+    assert np.array_equal(pl["token_req"], np.repeat(np.arange(bs), c).astype(np.int32))
+    seg = pl["segments"].reshape(-1, 4) if bs else np.zeros((0, 4), np.int32)
+    sp_all = pl["slot_pages"]
+    for r in range(bs):
+        toks = np.nonzero(pl["token_req"] == r)[0]
+        base = pl["topk_offsets"][toks]
+        assert np.all(base == seg[r, 2])
+        assert seg[r, 0] == (toks[0] if len(toks) else seg[r, 0]) and seg[r, 1] == c[r]
+        assert seg[r, 3] == pl["kv_lens"][r] and seg[r, 2] == pl["k_bases"][r]
+        for jj, t in enumerate(toks):
+            row = base[jj] + PS * P[r] + jj
+            assert kind[row] == KIND_CUR and idx[row] == t
+        for x in range(0, PS * P[r], max(1, PS // 2)):
+            row = seg[r, 2] + x
+            assert kind[row] == KIND_POOL
+            assert idx[row] == sp_all[ps_[r, 0] + x // PS] * PS + x % PS
+    at = 0
+    for r in range(bs):
+        assert seg[r, 0] == at
+        at += c[r]
+
     # dense bases: each request owns rows [k_bases, k_bases + PS*n_r); its
     # current rows start at current_bases; kv_lens counts its non-pad rows
     for r in range(bs):
@@ -252,6 +277,52 @@ def pin_library_routines(batch, pl, pool, cur, dense, staging):
             assert np.array_equal(dense[a * PS:b * PS], want)
 
 
+def pin_prefetch_split(orc, batch, pl, pool, cur, dense, staging):
+    """The layer-ahead split (page 0d87bc5, commit "prefetch staging
+    exchange"): the prefix slots and the current slots partition the dense
+    slots; gathering the prefix slots first and the current slots second
+    reproduces the one-shot gather and leaves the other half untouched; the
+    fused fill writes every current row to its staging row and to its pool
+    location, and the pool location is the pool row the dense buffer shows
+    for that token's page."""
+    PS, RB = batch.page_size, batch.row_bytes
+    NP = batch.n_pool_entries
+    S = dense.shape[0] // PS
+    kind, idx = decode(dense)
+    pre, cur_s = pl["prefix_slots"], pl["current_slots"]
+    assert len(pre) + len(cur_s) == S
+    assert np.array_equal(np.sort(np.concatenate([pre, cur_s])), np.arange(S))
+    assert np.all(np.diff(pre) > 0) and np.all(np.diff(cur_s) > 0)
+    for s in pre:
+        assert np.all(kind[s * PS:(s + 1) * PS] == KIND_POOL)
+    for i, s in enumerate(cur_s):
+        assert np.all(kind[s * PS:(s + 1) * PS] != KIND_POOL)
+        assert pl["owner"][s] >= NP and pl["src"][s] == i + 1
+    ml = pl["mixed_locs"].astype(np.int64)
+    locs = pl["pool_locs"].astype(np.int64)
+    assert np.array_equal(locs // PS, pl["slot_pages"][ml // PS])
+    assert np.array_equal(locs % PS, ml % PS)
+
+    table = oracle.pointer_table(pool, staging.reshape(-1), NP, batch.n_writers,
+                                 batch.staging_cap_pages, PS, RB)
+    split = np.full_like(dense, 0xEE)
+    assert not orc.gather_slots(table, pre, pl["owner"], pl["src"], PS, RB, split)
+    for s in cur_s:
+        assert np.all(split[s * PS:(s + 1) * PS] == 0xEE), "prefix gather touched a current slot"
+    assert not orc.gather_slots(table, cur_s, pl["owner"], pl["src"], PS, RB, split)
+    assert np.array_equal(split, dense), "split gather != one-shot gather"
+
+    st = np.zeros(batch.staging_rows_total * RB, np.uint8)
+    pool2 = pool.copy()
+    assert not orc.fill(st, pl["staging_rows"], pool2.reshape(-1), pl["pool_locs"], cur, RB)
+    assert np.array_equal(st.reshape(-1, RB), staging), "fill staging != scatter staging"
+    touched = np.zeros(pool.shape[0], bool)
+    touched[locs] = True
+    assert np.array_equal(pool2[~touched], pool[~touched])
+    pk, pi = decode(pool2[locs])
+    assert np.all(pk == KIND_CUR) and np.array_equal(pi, np.arange(len(locs)))
+
+
 def check_batch(orc, batch):
     """All per-batch pins on one batch."""
     pool, cur = tagged_values(batch)
@@ -260,6 +331,7 @@ def check_batch(orc, batch):
     pin_closed_form(batch, pool, cur, dense)
     pin_plan_geometry(batch, pl, dense, staging)
     pin_library_routines(batch, pl, pool, cur, dense, staging)
+    pin_prefetch_split(orc, batch, pl, pool, cur, dense, staging)
 
 
 def pin_tiny_worked(orc):
