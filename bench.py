@@ -44,6 +44,9 @@ def _args():
                     help="write profiles/ summaries from three rocprofv3 csv output "
                          "directories (kernel trace + stats, FETCH_SIZE, WRITE_SIZE) "
                          "and exit; runs on the host only")
+    ap.add_argument("--twin-index-bytes", type=int, default=144,
+                    help="also time the indexer-key twin compose with rows of this "
+                         "many bytes on the same plan (0 disables it)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="end with three torch copies of this size (counter "
                          "calibration under rocprofv3)")
@@ -296,6 +299,40 @@ def main():
                        "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": _traffic(a.workload, g_bytes),
                        "kernel": "compose_gather", "bytes_per_launch": g_bytes}
+    # layer-ahead prefetch split: the prefix gather can run a layer ahead, so
+    # the per-layer critical path is the fill (or scatter) plus the gather of
+    # the current pages only
+    pre_ms = _timed(stream, lambda: [runner.gather_prefix(l, stream) for l in range(L)],
+                    reps) / L
+    cur_ms = _timed(stream, lambda: [runner.gather_current(l, stream) for l in range(L)],
+                    reps) / L
+    fill_ms = _timed(stream, lambda: [runner.fill(l, stream) for l in range(L)], reps) / L
+    out["prefetch_split"] = {
+        "prefix_gather_us": round(pre_ms * 1e3, 2),
+        "current_gather_us": round(cur_ms * 1e3, 2),
+        "fused_fill_us": round(fill_ms * 1e3, 2),
+        "consume_us": round((s_ms + cur_ms) * 1e3, 2),
+        "consume_with_fused_fill_us": round((fill_ms + cur_ms) * 1e3, 2),
+        "fused_fill_bytes": 3 * batch.n_cur_tokens * batch.row_bytes
+                            + 8 * batch.n_cur_tokens}
+    if a.twin_index_bytes:
+        rb = a.twin_index_bytes
+        ipools, icurs = workloads.make_values(batch, device="cuda", row_bytes=rb,
+                                              value_kind="bytes", seed=batch.seed + 1)
+        twin = gpb.ComposeRunner(
+            gpb.BatchMeta(batch.bs, batch.page_size, rb, batch.n_pool_pages,
+                          batch.n_pool_entries, batch.n_writers, batch.staging_cap_pages,
+                          batch.prefix_pages, batch.cur_tokens, batch.req_pages),
+            ipools, icurs, plan=runner.plan)
+        twin.begin_batch(stream)
+        t_ms = _timed(stream, lambda: [twin.layer(l, stream) for l in range(L)], reps) / L
+        tb = twin.algorithmic_bytes_per_layer()
+        out["index_twin"] = {"row_bytes": rb, "us_per_layer": round(t_ms * 1e3, 2),
+                             "algorithmic_bytes_per_layer": tb,
+                             "gbs": round(tb / (t_ms * 1e-3) / 1e9, 1)}
+        assert int(twin.status.item()) == 0
+        del ipools, icurs, twin
+    assert int(runner.status.item()) == 0
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib << 20
         x = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -37,7 +37,8 @@ class gpb_batch(ctypes.Structure):
 PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
                "q_starts", "k_bases", "q_bases", "current_bases", "slot_pages",
                "owner", "src", "page_inverse", "staging_page_inverse", "writer",
-               "staging_rows", "mixed_locs")
+               "staging_rows", "mixed_locs", "token_req", "topk_offsets", "segments",
+               "prefix_slots", "current_slots", "pool_locs")
 
 
 class gpb_plan(ctypes.Structure):
@@ -85,10 +86,14 @@ def _load(path):
     lib.gpb_current_row_scatter.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp]
     lib.gpb_compose_gather.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, vp, i32,
                                        i32, i32, vp, vp]
+    lib.gpb_compose_gather_slots.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, i32, vp,
+                                             vp, i32, i32, i32, vp, vp]
+    lib.gpb_current_row_fill.argtypes = [vp, i64, vp, vp, i64, vp, vp, i32, i32, vp, vp]
     lib.gpb_strerror.argtypes = [ctypes.c_int]
     lib.gpb_strerror.restype = ctypes.c_char_p
     for f in ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
-              "gpb_current_row_scatter", "gpb_compose_gather"):
+              "gpb_current_row_scatter", "gpb_compose_gather",
+              "gpb_compose_gather_slots", "gpb_current_row_fill"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -96,7 +101,8 @@ def _load(path):
 lib = _load(LIB_PATH)
 
 EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
-           "gpb_current_row_scatter", "gpb_compose_gather", "gpb_strerror")
+           "gpb_current_row_scatter", "gpb_compose_gather", "gpb_compose_gather_slots",
+           "gpb_current_row_fill", "gpb_strerror")
 
 
 class GpbError(RuntimeError):
@@ -192,7 +198,10 @@ class Plan:
                  "q_bases": bs, "current_bases": bs, "slot_pages": self.S,
                  "owner": self.S, "src": self.S, "page_inverse": npp,
                  "staging_page_inverse": npp, "writer": self.NCP,
-                 "staging_rows": self.T, "mixed_locs": self.T}
+                 "staging_rows": self.T, "mixed_locs": self.T, "token_req": self.T,
+                 "topk_offsets": self.T, "segments": 4 * bs,
+                 "prefix_slots": self.S - self.NCP, "current_slots": self.NCP,
+                 "pool_locs": self.T}
         self.t = {k: torch.empty(sizes[k], dtype=torch.int32, device=dev)
                   for k in PLAN_FIELDS}
         self.c = gpb_plan(*[(self.t[k].data_ptr() if sizes[k] else None)
@@ -248,3 +257,25 @@ def compose_gather(dense, sources, owner, src, n_slots, page_rows, row_bytes,
                                   _ptr(src), int(n_slots), int(page_rows),
                                   int(row_bytes), _ptr(status), _stream(stream)),
            "gpb_compose_gather")
+
+
+def compose_gather_slots(dense, sources, slots, n_list, owner, src, n_slots, page_rows,
+                         row_bytes, status=None, stream=None):
+    """Gather only the listed dense slots (prefetch or consume half)."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_gather_slots(_ptr(dense), ctypes.byref(sources.c), _ptr(slots),
+                                        int(n_list), _ptr(owner), _ptr(src), int(n_slots),
+                                        int(page_rows), int(row_bytes), _ptr(status),
+                                        _stream(stream)),
+           "gpb_compose_gather_slots")
+
+
+def current_row_fill(staging, n_staging_rows, staging_rows, pool, n_pool_rows, pool_locs,
+                     cur_rows, n_rows, row_bytes, status=None, stream=None):
+    """Each current row to its staging row and to its pool row, one pass."""
+    _check(lib.gpb_current_row_fill(_ptr(staging), int(n_staging_rows), _ptr(staging_rows),
+                                    _ptr(pool), int(n_pool_rows), _ptr(pool_locs),
+                                    _ptr(cur_rows), int(n_rows), int(row_bytes),
+                                    _ptr(status), _stream(stream)),
+           "gpb_current_row_fill")

@@ -79,14 +79,23 @@ __device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t
 // slot's descriptor is uniform across the workgroup: owner/src are scalar
 // loads and both buffer resources live in scalar registers.  Lane l moves
 // chunks l, l + B, ... of the unit.  An invalid or -1 descriptor gets a
-// source range of 0 bytes: every load returns zeros.
-template <int B, int CPT>
+// source range of 0 bytes: every load returns zeros.  With LIST, the k-th
+// group of units serves dense slot slots[k] instead of slot k.
+template <int B, int CPT, bool LIST>
 __global__ __launch_bounds__(B) void k_compose_gather(
-    uint8_t *__restrict__ dense, SrcTable tbl, const int32_t *__restrict__ owner,
-    const int32_t *__restrict__ src, int32_t page_bytes, int32_t parts,
-    int32_t *status) {
-  const int slot = blockIdx.x / parts;
-  const int part = blockIdx.x - slot * parts;
+    uint8_t *__restrict__ dense, SrcTable tbl, const int32_t *__restrict__ slots,
+    int32_t n_slots, const int32_t *__restrict__ owner, const int32_t *__restrict__ src,
+    int32_t page_bytes, int32_t parts, int32_t *status) {
+  const int k_unit = blockIdx.x / parts;
+  const int part = blockIdx.x - k_unit * parts;
+  int slot = k_unit;
+  if (LIST) {
+    slot = slots[k_unit];
+    if (slot < 0 || slot >= n_slots) {
+      if (status && part == 0 && threadIdx.x == 0) atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+      return;
+    }
+  }
   const int e = owner[slot];
   const int p = src[slot];
   const bool sentinel = (e < 0) || (p < 0);
@@ -111,11 +120,14 @@ __global__ __launch_bounds__(B) void k_compose_gather(
 // divides once.  Consecutive lanes read consecutive source chunks; the
 // destination row of each chunk comes from staging_rows.  Chunks past the
 // last row read zeros and their stores go to kDropOffset (dropped), as do
-// rows whose staging row is out of range.
-template <int B, int CPT>
+// rows whose staging row is out of range.  With FILL, each chunk is also
+// written to its row of the pool (pool_locs), with a 64-bit address since a
+// pool may exceed one buffer range.
+template <int B, int CPT, bool FILL>
 __global__ __launch_bounds__(B) void k_row_scatter(
     uint8_t *__restrict__ staging, int32_t staging_bytes, int32_t n_staging_rows,
-    const int32_t *__restrict__ rows, const uint8_t *__restrict__ cur,
+    const int32_t *__restrict__ rows, u32x4 *__restrict__ pool, int64_t n_pool_rows,
+    const int32_t *__restrict__ pool_locs, const uint8_t *__restrict__ cur,
     int32_t n_rows, int32_t row_chunks, int32_t step_rows, int32_t step_off,
     int32_t *status) {
   const __amdgpu_buffer_rsrc_t rs = rsrc(cur, n_rows * row_chunks * 16);
@@ -125,15 +137,23 @@ __global__ __launch_bounds__(B) void k_row_scatter(
   int off = g - row * row_chunks;
   u32x4 v[CPT];
   uint32_t dst[CPT];
+  int64_t pdst[CPT];
   bool bad = false;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     const bool live = row < n_rows;
-    const int d = rows[live ? row : n_rows - 1];
+    const int last = live ? row : n_rows - 1;
+    const int d = rows[last];
     const bool ok = live && d >= 0 && d < n_staging_rows;
     bad |= live && !ok;
     v[k] = ld16(rs, static_cast<uint32_t>(row * row_chunks + off) * 16u);
     dst[k] = ok ? static_cast<uint32_t>(d * row_chunks + off) * 16u : kDropOffset;
+    if (FILL) {
+      const int64_t q = pool_locs[last];
+      const bool okp = live && q >= 0 && q < n_pool_rows;
+      bad |= live && !okp;
+      pdst[k] = okp ? q * row_chunks + off : -1;
+    }
     off += step_off;
     row += step_rows;
     if (off >= row_chunks) {
@@ -142,7 +162,10 @@ __global__ __launch_bounds__(B) void k_row_scatter(
     }
   }
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) st16(v[k], rd, dst[k]);
+  for (int k = 0; k < CPT; ++k) {
+    st16(v[k], rd, dst[k]);
+    if (FILL && pdst[k] >= 0) __builtin_nontemporal_store(v[k], pool + pdst[k]);
+  }
   if (bad && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
 }
 
@@ -174,21 +197,25 @@ extern "C" int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream) {
                 as_stream(stream), static_cast<u32x4 *>(d_ptr), chunks);
 }
 
-extern "C" int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
-                                       const int32_t *d_staging_rows,
-                                       const void *d_cur_rows, int32_t n_rows,
-                                       int32_t row_bytes, int32_t *d_status,
-                                       void *stream) {
-  using namespace gpb;
+namespace gpb {
+namespace {
+
+int launch_rows(void *d_staging, int64_t n_staging_rows, const int32_t *d_staging_rows,
+                void *d_pool, int64_t n_pool_rows, const int32_t *d_pool_locs,
+                const void *d_cur_rows, int32_t n_rows, int32_t row_bytes,
+                int32_t *d_status, void *stream, bool fill) {
   constexpr int B = GPB_SCATTER_BLOCK, CPT = GPB_SCATTER_CPT;
   if (n_rows < 0 || n_staging_rows < 0 || row_bytes < 1) return GPB_EINVAL;
+  if (fill && n_pool_rows < 0) return GPB_EINVAL;
   if (n_staging_rows > INT32_MAX) return GPB_ERANGE;
   if (row_bytes % 16 != 0) return GPB_EALIGN;
   if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
   if (n_rows == 0) return GPB_OK;
   if (!d_staging || !d_staging_rows || !d_cur_rows) return GPB_EINVAL;
+  if (fill && (!d_pool || !d_pool_locs)) return GPB_EINVAL;
   if (!aligned(d_staging, 16) || !aligned(d_cur_rows, 16) || !aligned(d_staging_rows, 4))
     return GPB_EALIGN;
+  if (fill && (!aligned(d_pool, 16) || !aligned(d_pool_locs, 4))) return GPB_EALIGN;
   const int64_t row_chunks = row_bytes / 16;
   // buffer ranges are 32-bit byte counts: both regions must stay below 2 GiB
   const int64_t cur_bytes = static_cast<int64_t>(n_rows) * row_bytes;
@@ -196,10 +223,62 @@ extern "C" int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
   if (cur_bytes > INT32_MAX || staging_bytes > INT32_MAX) return GPB_ERANGE;
   const int64_t total = static_cast<int64_t>(n_rows) * row_chunks;
   const int64_t grid = ceil_div64(total, static_cast<int64_t>(B) * CPT);
-  return launch(k_row_scatter<B, CPT>, dim3(static_cast<uint32_t>(grid)), dim3(B),
-                as_stream(stream), d_staging, staging_bytes, n_staging_rows,
-                d_staging_rows, d_cur_rows, n_rows, row_chunks, B / row_chunks,
-                B % row_chunks, d_status);
+  const dim3 g(static_cast<uint32_t>(grid)), b(B);
+  hipStream_t st = as_stream(stream);
+  if (fill)
+    return launch(k_row_scatter<B, CPT, true>, g, b, st, d_staging, staging_bytes,
+                  n_staging_rows, d_staging_rows, d_pool, n_pool_rows, d_pool_locs,
+                  d_cur_rows, n_rows, row_chunks, B / row_chunks, B % row_chunks, d_status);
+  return launch(k_row_scatter<B, CPT, false>, g, b, st, d_staging, staging_bytes,
+                n_staging_rows, d_staging_rows, nullptr, 0, nullptr, d_cur_rows, n_rows,
+                row_chunks, B / row_chunks, B % row_chunks, d_status);
+}
+
+// Host checks shared by the two gathers; fills the kernel's table.
+int check_gather(const gpb_sources *table, int32_t n_slots, int32_t page_rows,
+                 int32_t row_bytes, int32_t *d_status, SrcTable *t, int64_t *page_bytes) {
+  if (!table || n_slots < 0 || page_rows < 1 || row_bytes < 1) return GPB_EINVAL;
+  if (table->n < 1 || table->n > GPB_MAX_SOURCES) return GPB_EINVAL;
+  if (row_bytes % 16 != 0) return GPB_EALIGN;
+  if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
+  *page_bytes = static_cast<int64_t>(page_rows) * row_bytes;
+  // a page is one buffer range: 32-bit byte count, with room for the last unit
+  if (*page_bytes > INT32_MAX - (1 << 20)) return GPB_ERANGE;
+  t->n = table->n;
+  for (int e = 0; e < GPB_MAX_SOURCES; ++e) {
+    t->base[e] = nullptr;
+    t->n_pages[e] = 0;
+  }
+  for (int e = 0; e < table->n; ++e) {
+    if (table->n_pages[e] < 0) return GPB_EINVAL;
+    if (table->n_pages[e] > 0 && !table->base[e]) return GPB_EINVAL;
+    if (!aligned(table->base[e], 16)) return GPB_EALIGN;
+    t->base[e] = static_cast<const uint8_t *>(table->base[e]);
+    t->n_pages[e] = table->n_pages[e];
+  }
+  return GPB_OK;
+}
+
+}  // namespace
+}  // namespace gpb
+
+extern "C" int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
+                                       const int32_t *d_staging_rows,
+                                       const void *d_cur_rows, int32_t n_rows,
+                                       int32_t row_bytes, int32_t *d_status,
+                                       void *stream) {
+  return gpb::launch_rows(d_staging, n_staging_rows, d_staging_rows, nullptr, 0, nullptr,
+                          d_cur_rows, n_rows, row_bytes, d_status, stream, false);
+}
+
+extern "C" int gpb_current_row_fill(void *d_staging, int64_t n_staging_rows,
+                                    const int32_t *d_staging_rows, void *d_pool,
+                                    int64_t n_pool_rows, const int32_t *d_pool_locs,
+                                    const void *d_cur_rows, int32_t n_rows,
+                                    int32_t row_bytes, int32_t *d_status, void *stream) {
+  return gpb::launch_rows(d_staging, n_staging_rows, d_staging_rows, d_pool, n_pool_rows,
+                          d_pool_locs, d_cur_rows, n_rows, row_bytes, d_status, stream,
+                          true);
 }
 
 extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
@@ -209,34 +288,45 @@ extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
                                   void *stream) {
   using namespace gpb;
   constexpr int B = GPB_GATHER_BLOCK, CPT = GPB_GATHER_CPT;
-  if (!table || n_slots < 0 || page_rows < 1 || row_bytes < 1) return GPB_EINVAL;
-  if (table->n < 1 || table->n > GPB_MAX_SOURCES) return GPB_EINVAL;
-  if (row_bytes % 16 != 0) return GPB_EALIGN;
-  if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
-  const int64_t page_bytes = static_cast<int64_t>(page_rows) * row_bytes;
-  // a page is one buffer range: 32-bit byte count, with room for the last unit
-  if (page_bytes > INT32_MAX - (1 << 20)) return GPB_ERANGE;
   SrcTable t;
-  t.n = table->n;
-  for (int e = 0; e < GPB_MAX_SOURCES; ++e) {
-    t.base[e] = nullptr;
-    t.n_pages[e] = 0;
-  }
-  for (int e = 0; e < table->n; ++e) {
-    if (table->n_pages[e] < 0) return GPB_EINVAL;
-    if (table->n_pages[e] > 0 && !table->base[e]) return GPB_EINVAL;
-    if (!aligned(table->base[e], 16)) return GPB_EALIGN;
-    t.base[e] = static_cast<const uint8_t *>(table->base[e]);
-    t.n_pages[e] = table->n_pages[e];
-  }
+  int64_t page_bytes = 0;
+  int rc = check_gather(table, n_slots, page_rows, row_bytes, d_status, &t, &page_bytes);
+  if (rc != GPB_OK) return rc;
   if (n_slots == 0) return GPB_OK;
   if (!d_dense || !d_owner || !d_src) return GPB_EINVAL;
   if (!aligned(d_dense, 16) || !aligned(d_owner, 4) || !aligned(d_src, 4)) return GPB_EALIGN;
   const int64_t parts = ceil_div64(page_bytes / 16, static_cast<int64_t>(B) * CPT);
   const int64_t grid = parts * n_slots;
   if (grid > INT32_MAX) return GPB_ERANGE;
-  return launch(k_compose_gather<B, CPT>, dim3(static_cast<uint32_t>(grid)), dim3(B),
-                as_stream(stream), d_dense, t, d_owner, d_src, page_bytes, parts, d_status);
+  return launch(k_compose_gather<B, CPT, false>, dim3(static_cast<uint32_t>(grid)), dim3(B),
+                as_stream(stream), d_dense, t, nullptr, n_slots, d_owner, d_src,
+                page_bytes, parts, d_status);
+}
+
+extern "C" int gpb_compose_gather_slots(void *d_dense, const gpb_sources *table,
+                                        const int32_t *d_slots, int32_t n_list,
+                                        const int32_t *d_owner, const int32_t *d_src,
+                                        int32_t n_slots, int32_t page_rows,
+                                        int32_t row_bytes, int32_t *d_status,
+                                        void *stream) {
+  using namespace gpb;
+  constexpr int B = GPB_GATHER_BLOCK, CPT = GPB_GATHER_CPT;
+  SrcTable t;
+  int64_t page_bytes = 0;
+  int rc = check_gather(table, n_slots, page_rows, row_bytes, d_status, &t, &page_bytes);
+  if (rc != GPB_OK) return rc;
+  if (n_list < 0) return GPB_EINVAL;
+  if (n_list == 0) return GPB_OK;
+  if (!d_dense || !d_owner || !d_src || !d_slots || n_slots == 0) return GPB_EINVAL;
+  if (!aligned(d_dense, 16) || !aligned(d_owner, 4) || !aligned(d_src, 4) ||
+      !aligned(d_slots, 4))
+    return GPB_EALIGN;
+  const int64_t parts = ceil_div64(page_bytes / 16, static_cast<int64_t>(B) * CPT);
+  const int64_t grid = parts * n_list;
+  if (grid > INT32_MAX) return GPB_ERANGE;
+  return launch(k_compose_gather<B, CPT, true>, dim3(static_cast<uint32_t>(grid)), dim3(B),
+                as_stream(stream), d_dense, t, d_slots, n_slots, d_owner, d_src,
+                page_bytes, parts, d_status);
 }
 
 namespace gpb {

@@ -16,9 +16,11 @@
 //      spans and ragged descriptors; the other workgroups fill both page
 //      inverses with -1.
 //   2. k_plan_slots: one lane per dense slot -> slot page, page inverse,
-//      gather descriptor, writer and staging page inverse.
+//      gather descriptor, writer, staging page inverse, and the slot's place
+//      in the prefix or current slot list.
 //   3. k_plan_tokens: one lane per current token -> staging row through the
-//      staging page inverse, and mixed_locs.
+//      staging page inverse, mixed_locs, the per-token expansions (request
+//      row id, top-k offset) and the token's pool row.
 // Request lookups in 2 and 3 are binary searches over the scanned bases,
 // staged in LDS.
 #include <algorithm>
@@ -38,6 +40,8 @@ struct PlanArgs {
   int32_t *q_lens, *kv_lens, *q_starts, *k_bases, *q_bases, *current_bases;
   int32_t *slot_pages, *owner, *src, *page_inverse, *staging_page_inverse;
   int32_t *writer, *staging_rows, *mixed_locs;
+  int32_t *token_req, *topk_offsets, *segments;
+  int32_t *prefix_slots, *current_slots, *pool_locs;
 };
 
 // Inclusive scan across one wave64 (Hillis-Steele over lane shuffles).
@@ -100,6 +104,10 @@ __device__ void scan_requests(const PlanArgs &a) {
       a.k_bases[r] = a.ps * ex_n;
       a.current_bases[r] = a.ps * (ex_n + P);
       a.q_bases[r] = a.ps * ex_C;
+      a.segments[4 * r] = ex_c;
+      a.segments[4 * r + 1] = c;
+      a.segments[4 * r + 2] = a.ps * ex_n;
+      a.segments[4 * r + 3] = a.ps * P + c;
     }
     carry_n = all_n;
     carry_c = all_c;
@@ -154,22 +162,25 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
   const int page = a.req_pages[s];
   a.slot_pages[s] = page;
   a.page_inverse[page] = s;
+  const int cur_before = qb[r] / a.ps;  // current pages of earlier requests
   if (j < P) {  // prefix slot: modulo-owned pool entry, the page itself
     a.owner[s] = page % a.np;
     a.src[s] = page;
+    a.prefix_slots[s - cur_before] = s;
   } else {      // current page i of the batch
-    const int i = qb[r] / a.ps + (j - P);
+    const int i = cur_before + (j - P);
     const int w = i % a.w;
     a.writer[i] = w;
     a.owner[s] = a.np + w;
     a.src[s] = i + 1;
     a.staging_page_inverse[page] = w * a.cap + i + 1;
+    a.current_slots[i] = s;
   }
 }
 
 __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   __shared__ int32_t s_qs[kLdsRequests], s_base[kLdsRequests], s_P[kLdsRequests],
-      s_cb[kLdsRequests];
+      s_cb[kLdsRequests], s_kb[kLdsRequests];
   const bool lds = a.bs <= kLdsRequests;
   if (lds) {
     for (int r = threadIdx.x; r < a.bs; r += kBlock) {
@@ -177,6 +188,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
       s_base[r] = a.slot_base[r];
       s_P[r] = a.P[r];
       s_cb[r] = a.current_bases[r];
+      s_kb[r] = a.k_bases[r];
     }
     __syncthreads();
   }
@@ -184,6 +196,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   const int32_t *base = lds ? s_base : a.slot_base;
   const int32_t *Pv = lds ? s_P : a.P;
   const int32_t *cb = lds ? s_cb : a.current_bases;
+  const int32_t *kb = lds ? s_kb : a.k_bases;
   const int t = blockIdx.x * kBlock + threadIdx.x;
   if (t >= a.n_rows) return;
   const int r = find_request(qs, a.bs, t);
@@ -193,6 +206,9 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   const int spage = a.staging_page_inverse[loc / a.ps];
   a.staging_rows[t] = spage * a.ps + loc % a.ps;
   a.mixed_locs[t] = cb[r] + j;
+  a.token_req[t] = r;
+  a.topk_offsets[t] = kb[r];
+  a.pool_locs[t] = loc;
 }
 
 // Host-side validation of a batch; the rules and their order match the
@@ -258,7 +274,9 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
       {o->d_k_bases, bs}, {o->d_q_bases, bs}, {o->d_current_bases, bs},
       {o->d_slot_pages, S}, {o->d_owner, S}, {o->d_src, S},
       {o->d_page_inverse, npp}, {o->d_staging_page_inverse, npp},
-      {o->d_writer, NCP}, {o->d_staging_rows, T}, {o->d_mixed_locs, T}};
+      {o->d_writer, NCP}, {o->d_staging_rows, T}, {o->d_mixed_locs, T},
+      {o->d_token_req, T}, {o->d_topk_offsets, T}, {o->d_segments, 4 * bs},
+      {o->d_prefix_slots, S - NCP}, {o->d_current_slots, NCP}, {o->d_pool_locs, T}};
   for (const Need &e : need) {
     if (e.n > 0 && !e.p) return GPB_EINVAL;
     if (!ok_array(e.p, e.n)) return GPB_EALIGN;
@@ -275,6 +293,10 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
   a.owner = o->d_owner; a.src = o->d_src; a.page_inverse = o->d_page_inverse;
   a.staging_page_inverse = o->d_staging_page_inverse; a.writer = o->d_writer;
   a.staging_rows = o->d_staging_rows; a.mixed_locs = o->d_mixed_locs;
+  a.token_req = o->d_token_req; a.topk_offsets = o->d_topk_offsets;
+  a.segments = o->d_segments;
+  a.prefix_slots = o->d_prefix_slots; a.current_slots = o->d_current_slots;
+  a.pool_locs = o->d_pool_locs;
 
   hipStream_t st = as_stream(stream);
   // workgroup 0 scans; the rest fill the inverses (4 entries per lane-pass)

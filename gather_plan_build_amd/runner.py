@@ -25,13 +25,28 @@ class ComposeRunner:
     pools[k], curs[k]: uint8 device tensors [rows, row_bytes]; layer l uses
     index l mod len(pools)."""
 
-    def __init__(self, meta, pools, curs, device="cuda"):
+    def __init__(self, meta, pools, curs, device="cuda", plan=None):
         b = meta.c
         self.meta = meta
         self.ps, self.rb = b.page_size, b.row_bytes
         self.np_, self.w, self.cap = b.n_pool_entries, b.n_writers, b.staging_cap_pages
         self.n_pool_pages = b.n_pool_pages
-        self.plan = B.Plan(meta, device)
+        if plan is None:
+            plan = B.Plan(meta, device)
+        else:
+            # a twin row format (e.g. indexer keys next to token KV) reuses the
+            # batch's plan: no plan array depends on the row size
+            B.plan_sizes(meta)
+            m = plan.meta.c
+            assert (m.bs, m.page_size, m.n_pool_pages, m.n_pool_entries, m.n_writers,
+                    m.staging_cap_pages) == (b.bs, b.page_size, b.n_pool_pages,
+                                             b.n_pool_entries, b.n_writers,
+                                             b.staging_cap_pages)
+            assert (plan.meta.h_prefix == meta.h_prefix).all()
+            assert (plan.meta.h_cur == meta.h_cur).all()
+            assert (plan.meta.h_req == meta.h_req).all()
+        self.plan = plan
+        self.owns_plan = plan.meta is meta
         self.S, self.T = self.plan.S, self.plan.T
         self.pools, self.curs = list(pools), list(curs)
         for p in self.pools:
@@ -60,8 +75,10 @@ class ComposeRunner:
                 self.tables[(k, h)] = B.Sources(entries)
 
     def begin_batch(self, stream=None):
-        """Plan build + clear of both staging halves (once per batch)."""
-        self.plan.build(stream)
+        """Plan build (unless the plan belongs to a twin) + clear of both
+        staging halves (once per batch)."""
+        if self.owns_plan:
+            self.plan.build(stream)
         for h in range(PARITY):
             B.staging_clear(self.staging[h], stream=stream)
 
@@ -80,6 +97,45 @@ class ComposeRunner:
     def layer(self, layer, stream=None):
         self.scatter(layer, stream)
         self.gather(layer, stream)
+
+    # Layer-ahead prefetch split (page 0d87bc5, commit "prefetch staging
+    # exchange"): the prefix pages of a layer's dense buffer can be gathered
+    # ahead of time; the consume step is the scatter (or the fused fill) and
+    # the gather of the current pages only.
+
+    def gather_prefix(self, layer, stream=None):
+        h, k = layer % PARITY, layer % len(self.pools)
+        t = self.plan.t
+        B.compose_gather_slots(self.dense[h], self.tables[(k, h)], t["prefix_slots"],
+                               self.S - self.plan.NCP, t["owner"], t["src"], self.S,
+                               self.ps, self.rb, self.status, stream)
+
+    def gather_current(self, layer, stream=None):
+        h, k = layer % PARITY, layer % len(self.pools)
+        t = self.plan.t
+        B.compose_gather_slots(self.dense[h], self.tables[(k, h)], t["current_slots"],
+                               self.plan.NCP, t["owner"], t["src"], self.S, self.ps,
+                               self.rb, self.status, stream)
+
+    def fill(self, layer, stream=None):
+        """Fused current fill: current rows to staging and to their pool rows
+        in the layer's pool arena."""
+        h, k = layer % PARITY, layer % len(self.curs)
+        pool = self.pools[layer % len(self.pools)]
+        B.current_row_fill(self.staging[h], self.staging_rows_total,
+                           self.plan.t["staging_rows"], pool,
+                           self.n_pool_pages * self.ps, self.plan.t["pool_locs"],
+                           self.curs[k], self.T, self.rb, self.status, stream)
+
+    def layer_split(self, layer, stream=None, fused_fill=False):
+        """One layer as prefetch (prefix gather) then consume (fill or
+        scatter, then the current-page gather)."""
+        self.gather_prefix(layer, stream)
+        if fused_fill:
+            self.fill(layer, stream)
+        else:
+            self.scatter(layer, stream)
+        self.gather_current(layer, stream)
 
     def run(self, n_layers, stream=None):
         self.begin_batch(stream)

@@ -128,7 +128,25 @@ typedef struct gpb_batch {
  *   writer[i]             i mod W (page-aligned round robin)          [NCP]
  *   staging_rows[t]       staging row of current token t, found through
  *                         staging_page_inverse                        [T]
- *   mixed_locs[t]         dense row of current token t                [T]  */
+ *   mixed_locs[t]         dense row of current token t                [T]
+ * Per-token ragged expansions (page d63fbd4, commit "cut per-layer CPU on the
+ * prefill launch path": the O(total-q-tokens) top-k offset list and segment
+ * records of the ragged index plan; page 0d87bc5, commit "flattened request
+ * row ids": row ids built once per batch instead of a per-layer
+ * repeat_interleave):
+ *   token_req[t]          request of current token t (flattened row id)  [T]
+ *   topk_offsets[t]       k_bases of that request: a request-relative KV
+ *                         position plus this offset is a dense row       [T]
+ *   segments[4r..4r+3]    (q_starts, q_lens, k_bases, kv_lens) of r     [4bs]
+ * Layer-ahead prefetch split (page 0d87bc5, commit "prefetch staging
+ * exchange": the prefix of the dense buffer is filled a layer ahead, the
+ * consume step fills current rows into staging and gathers all current
+ * pages from it):
+ *   prefix_slots[u]       dense slots of prefix pages, ascending  [S - NCP]
+ *   current_slots[i]      dense slot of current page i            [NCP]
+ *   pool_locs[t]          pool row (KV-cache location) of current token t:
+ *                         slot_pages[its slot] * page_size + j mod page_size
+ *                                                                       [T] */
 typedef struct gpb_plan {
   int32_t *d_slot_base, *d_prefix_span, *d_current_span;
   int32_t *d_q_lens, *d_kv_lens, *d_q_starts;
@@ -137,6 +155,8 @@ typedef struct gpb_plan {
   int32_t *d_page_inverse, *d_staging_page_inverse;
   int32_t *d_writer;
   int32_t *d_staging_rows, *d_mixed_locs;
+  int32_t *d_token_req, *d_topk_offsets, *d_segments;
+  int32_t *d_prefix_slots, *d_current_slots, *d_pool_locs;
 } gpb_plan;
 
 /* Pointer table of source arenas for one gather (page d63fbd4, commit
@@ -204,6 +224,31 @@ int gpb_compose_gather(void *d_dense, const gpb_sources *table,
                        const int32_t *d_owner, const int32_t *d_src,
                        int32_t n_slots, int32_t page_rows, int32_t row_bytes,
                        int32_t *d_status, void *stream);
+
+/* Per layer, the two halves of the layer-ahead prefetch split: as
+ * gpb_compose_gather, but only for the n_list dense slots d_slots[k] (for
+ * instance the plan's prefix_slots a layer ahead, then its current_slots
+ * after the scatter); other slots of d_dense are not touched.  n_slots is the
+ * number of slots d_dense, d_owner and d_src hold: a listed slot outside
+ * [0, n_slots) is skipped and GPB_STATUS_BAD_DESCRIPTOR is ORed into
+ * *d_status.  A slot must not be listed twice. */
+int gpb_compose_gather_slots(void *d_dense, const gpb_sources *table,
+                             const int32_t *d_slots, int32_t n_list,
+                             const int32_t *d_owner, const int32_t *d_src,
+                             int32_t n_slots, int32_t page_rows, int32_t row_bytes,
+                             int32_t *d_status, void *stream);
+
+/* Per layer, the fused current fill: each current row t goes, in one pass
+ * over the rows, to staging row d_staging_rows[t] (the scatter above) and to
+ * pool row d_pool_locs[t] of d_pool (its KV-cache location), whole rows of
+ * row_bytes.  A destination outside [0, n_staging_rows) or [0, n_pool_rows)
+ * is skipped there and GPB_STATUS_BAD_STAGING_ROW is ORed into *d_status.
+ * The staging region is below 2 GiB; the pool may be any size. */
+int gpb_current_row_fill(void *d_staging, int64_t n_staging_rows,
+                         const int32_t *d_staging_rows, void *d_pool,
+                         int64_t n_pool_rows, const int32_t *d_pool_locs,
+                         const void *d_cur_rows, int32_t n_rows, int32_t row_bytes,
+                         int32_t *d_status, void *stream);
 
 /* Static, human-readable name of a gpb_status value. */
 const char *gpb_strerror(int status);

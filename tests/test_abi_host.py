@@ -130,6 +130,25 @@ def test_gather_argument_checks():
     assert f(a, ctypes.byref(good.c), a, a, 4, 1 << 20, 4096, None, None) == B.ERANGE
 
 
+def test_slot_gather_and_fill_argument_checks():
+    g = B.lib.gpb_compose_gather_slots
+    a = 0x100000
+    good = B.Sources([(a, 10)])
+    assert g(a, ctypes.byref(good.c), a, 0, a, a, 4, 64, 1152, None, None) == B.OK
+    assert g(a, ctypes.byref(good.c), a, -1, a, a, 4, 64, 1152, None, None) == B.EINVAL
+    assert g(a, ctypes.byref(good.c), None, 3, a, a, 4, 64, 1152, None, None) == B.EINVAL
+    assert g(a, ctypes.byref(good.c), a + 2, 3, a, a, 4, 64, 1152, None, None) == B.EALIGN
+    assert g(a, ctypes.byref(good.c), a, 3, a, a, 0, 64, 1152, None, None) == B.EINVAL
+    assert g(a, None, a, 3, a, a, 4, 64, 1152, None, None) == B.EINVAL
+    f = B.lib.gpb_current_row_fill
+    assert f(a, 10, a, a, 100, a, a, 0, 1152, None, None) == B.OK
+    assert f(a, 10, a, None, 100, a, a, 4, 1152, None, None) == B.EINVAL
+    assert f(a, 10, a, a, -1, a, a, 4, 1152, None, None) == B.EINVAL
+    assert f(a, 10, a, a + 8, 100, a, a, 4, 1152, None, None) == B.EALIGN
+    assert f(a, 10, a, a, 100, a + 1, a, 4, 1152, None, None) == B.EALIGN
+    assert f(a, 10, a, a, 100, a, a, 4, 1000, None, None) == B.EALIGN
+
+
 def test_staging_clear_argument_checks():
     f = B.lib.gpb_staging_clear
     assert f(0x100000, 0, None) == B.OK

@@ -163,7 +163,45 @@ def test_multi_layer_workloads(orc, name):
     for layer in (b.n_layers - 2, b.n_layers - 1):
         _check_layer(b, r, layer, want, pools_np, curs_np, orc)
         _say("  layer", layer, "ok")
+    for layer, fused in ((0, False), (1, True)):
+        _check_split(b, r, layer, want, pools_np[layer % len(pools_np)],
+                     curs_np[layer % len(curs_np)], orc, fused_fill=fused)
+        _say("  split layer", layer, "fused fill" if fused else "scatter", "ok")
     assert _status(r) == 0
+
+
+def _check_split(batch, r, layer, want_plan, pool_np, cur_np, orc, fused_fill):
+    """Prefetch split on the GPU (prefix gather, then scatter or fused fill,
+    then the current gather) against the oracle: dense and staging equal the
+    one-shot layer; with the fused fill, the pool rows of the current tokens
+    hold them afterwards and no other pool row changed."""
+    dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
+    h = layer % 2
+    r.dense[h].fill_(0xEE)
+    r.gather_prefix(layer)
+    torch.cuda.synchronize()
+    got = _host(r.dense_of(layer))
+    PS = batch.page_size
+    for s in want_plan["current_slots"]:
+        assert (got[s * PS:(s + 1) * PS] == 0xEE).all(), "prefix gather wrote a current slot"
+    if fused_fill:
+        pool_before = pool_np.reshape(-1, batch.row_bytes)
+        pool_after = pool_before.copy()
+        st = np.zeros(batch.staging_rows_total * batch.row_bytes, np.uint8)
+        assert not orc.fill(st, want_plan["staging_rows"], pool_after.reshape(-1),
+                            want_plan["pool_locs"], cur_np, batch.row_bytes)
+        r.fill(layer)
+    else:
+        r.scatter(layer)
+    r.gather_current(layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(r.dense_of(layer)), dense), "split dense differs"
+    assert np.array_equal(_host(r.staging_of(layer)), staging), "split staging differs"
+    if fused_fill:
+        k = layer % len(r.pools)
+        assert np.array_equal(_host(r.pools[k]).reshape(-1, batch.row_bytes), pool_after), \
+            "fused fill pool differs"
+        r.pools[k].copy_(torch.from_numpy(pool_np.reshape(r.pools[k].shape)))
 
 
 def _random_case(orc, b, layers=2):
@@ -176,6 +214,8 @@ def _random_case(orc, b, layers=2):
     want = _check_plan(b, r, orc)
     for layer in range(max(0, layers - 2), layers):
         _check_layer(b, r, layer, want, [pool_np], [cur_np], orc)
+    _check_split(b, r, layers, want, pool_np, cur_np, orc, fused_fill=False)
+    _check_split(b, r, layers + 1, want, pool_np, cur_np, orc, fused_fill=True)
     assert _status(r) == 0
 
 
@@ -250,6 +290,29 @@ def test_sentinel_and_out_of_range_descriptors(orc):
     assert int(status.item()) == gpb.STATUS_BAD_DESCRIPTOR
 
 
+def test_slot_list_out_of_range_is_skipped(orc):
+    """A listed slot outside the dense buffer is skipped and flagged; the
+    others are gathered."""
+    gpb = _gpb()
+    PS, RB = 2, 32
+    rng = np.random.default_rng(13)
+    pool_np = rng.integers(1, 256, (6 * PS, RB), dtype=np.uint8)
+    pool = torch.from_numpy(pool_np).cuda()
+    owner = torch.zeros(4, dtype=torch.int32, device="cuda")
+    src = torch.tensor([1, 2, 3, 4], dtype=torch.int32, device="cuda")
+    dense = torch.full((4 * PS, RB), 0x33, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    slots = torch.tensor([2, 9, -1, 0], dtype=torch.int32, device="cuda")
+    gpb.compose_gather_slots(dense, [(pool, 6)], slots, 4, owner, src, 4, PS, RB, status)
+    torch.cuda.synchronize()
+    h = _host(dense).reshape(4, PS, RB)
+    want = np.full((4, PS, RB), 0x33, np.uint8)
+    want[2] = pool_np[3 * PS:4 * PS]
+    want[0] = pool_np[1 * PS:2 * PS]
+    assert np.array_equal(h, want)
+    assert int(status.item()) == gpb.STATUS_BAD_DESCRIPTOR
+
+
 def test_out_of_range_staging_rows_are_skipped(orc):
     gpb = _gpb()
     RB = 32
@@ -275,3 +338,37 @@ def test_staging_clear_zeroes_exactly(orc):
     h = _host(buf)
     assert not h[16:16 + 4096 * 37].any()
     assert (h[:16] == 0xEE).all() and (h[16 + 4096 * 37:] == 0xEE).all()
+
+
+def test_index_key_twin_shares_the_plan(orc):
+    """The indexer-key twin (page 0d87bc5, commit "prefetch staging exchange":
+    the index fill is pointed at the same staging page inverse) composes a
+    second row format with the token plan of the traced batch: 144-byte rows,
+    byte-exact against the oracle on four layers."""
+    gpb = _gpb()
+    b = workloads.make_batch("traced")
+    rb = workloads.INDEX_ROW_BYTES
+    pools, curs = workloads.make_values(b, device="cuda", rotations=2)
+    tok = _runner(b, pools, curs)
+    ipools, icurs = workloads.make_values(b, device="cuda", rotations=2, row_bytes=rb,
+                                          value_kind="bytes", seed=1)
+    twin = gpb.ComposeRunner(gpb.BatchMeta(b.bs, b.page_size, rb, b.n_pool_pages,
+                                           b.n_pool_entries, b.n_writers,
+                                           b.staging_cap_pages, b.prefix_pages,
+                                           b.cur_tokens, b.req_pages),
+                             ipools, icurs, plan=tok.plan)
+    tok.begin_batch()
+    twin.begin_batch()
+    bi = workloads.Batch(b.name, b.bs, b.page_size, rb, b.n_pool_pages, b.n_pool_entries,
+                         b.n_writers, b.staging_cap_pages, b.prefix_pages, b.cur_tokens,
+                         b.req_pages)
+    want = oracle.plan_for(bi, orc)
+    ipools_np = [_host(p) for p in ipools]
+    icurs_np = [_host(c) for c in icurs]
+    for layer in range(4):
+        tok.layer(layer)
+        twin.layer(layer)
+        torch.cuda.synchronize()
+        _check_layer(bi, twin, layer, want, ipools_np, icurs_np, orc)
+        _say("  twin layer", layer, "ok")
+    assert _status(twin) == 0 and _status(tok) == 0

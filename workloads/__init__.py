@@ -3,5 +3,5 @@
 This package draws random numbers and lays them out; it holds none of the
 compose method's arithmetic (no spans, scans, inverses or descriptors).
 """
-from .gen import (Batch, CONFIGS, make_batch, make_values, random_batch,  # noqa: F401
-                  staging_cap_for)
+from .gen import (Batch, CONFIGS, INDEX_ROW_BYTES, make_batch, make_values,  # noqa: F401
+                  random_batch, staging_cap_for)

@@ -176,14 +176,23 @@ def _fill(kind, rows, row_bytes, g, device):
     return out
 
 
-def make_values(batch, device="cpu", seed=None, rotations=None):
+# Rows of the indexer-key twin: a 128-byte fp8 key and a 4-byte fp32 scale per
+# token, padded to the 16-byte unit rows move in.  The pages do not give the
+# indexer row size; this is a parameter of the twin, not of the method.
+INDEX_ROW_BYTES = 144
+
+
+def make_values(batch, device="cpu", seed=None, rotations=None, row_bytes=None,
+                value_kind=None):
     """Pool arenas and current rows, ``rotations`` of each (layer l uses
     index l mod rotations).  Pools: uint8 [n_pool_pages*PS, RB] (bf16 N(0,1)
-    bit patterns, or uniform bytes); current rows: uint8 [T, RB]."""
+    bit patterns, or uniform bytes); current rows: uint8 [T, RB].  row_bytes
+    and value_kind override the batch's (the index-key twin uses bytes)."""
     rot = batch.n_rotations if rotations is None else rotations
+    rb = batch.row_bytes if row_bytes is None else row_bytes
+    kind = batch.value_kind if value_kind is None else value_kind
     g = _gen(device, batch.seed if seed is None else seed)
-    pools = [_fill(batch.value_kind, batch.n_pool_pages * batch.page_size,
-                   batch.row_bytes, g, device) for _ in range(rot)]
-    curs = [_fill(batch.value_kind, batch.n_cur_tokens, batch.row_bytes, g, device)
-            for _ in range(rot)]
+    pools = [_fill(kind, batch.n_pool_pages * batch.page_size, rb, g, device)
+             for _ in range(rot)]
+    curs = [_fill(kind, batch.n_cur_tokens, rb, g, device) for _ in range(rot)]
     return pools, curs
