@@ -44,6 +44,9 @@ def _args():
                     help="write profiles/ summaries from three rocprofv3 csv output "
                          "directories (kernel trace + stats, FETCH_SIZE, WRITE_SIZE) "
                          "and exit; runs on the host only")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the headline path only (no prefetch split, fused fill "
+                         "or twin): the mode the profiler runs use")
     ap.add_argument("--twin-index-bytes", type=int, default=144,
                     help="also time the indexer-key twin compose with rows of this "
                          "many bytes on the same plan (0 disables it)")
@@ -53,11 +56,17 @@ def _args():
     return ap.parse_args()
 
 
+# the sources the counters depend on: the per-layer kernels and what they
+# include from the library (plan kernels and host entry points elsewhere do
+# not change the gather's traffic)
+DIGEST_FILES = ("gather_plan_build_amd/csrc/compose.hip",
+                "gather_plan_build_amd/csrc/gpb_common.h")
+
+
 def _source_digest():
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gather_plan_build_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in DIGEST_FILES:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
@@ -139,23 +148,28 @@ def _csv_rows(directory, suffix):
 
 
 def _short(name):
+    """Kernel name without namespaces and parameter list; template arguments
+    kept (they tell the gather from the slot-list gather, the scatter from the
+    fused fill)."""
+    import re
     for key in ("k_compose_gather", "k_row_scatter", "k_fill_zero", "k_plan_scan_fill",
                 "k_plan_slots", "k_plan_tokens", "copyBuffer"):
         if key in name:
-            return key
+            m = re.search(key + r"(<[^>]*>)?", name)
+            return m.group(0).replace(" ", "")
     return name[:60]
 
 
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py "
-             "--steps 3 --warmup 1 --cpu-seconds 0",
+             "--steps 3 --warmup 1 --cpu-seconds 0 --no-extras",
     "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv "
              "-d $REPO/gpurun_out/prof_fetch -o fetch -- python3 $REPO/bench.py "
-             "--steps 1 --warmup 0 --cpu-seconds 0 --calibration-copy-mib 1024",
+             "--steps 1 --warmup 0 --cpu-seconds 0 --no-extras --calibration-copy-mib 1024",
     "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv "
              "-d $REPO/gpurun_out/prof_write -o write -- python3 $REPO/bench.py "
-             "--steps 1 --warmup 0 --cpu-seconds 0 --calibration-copy-mib 1024",
+             "--steps 1 --warmup 0 --cpu-seconds 0 --no-extras --calibration-copy-mib 1024",
     "summary": "python3 bench.py --summarize-profiles gpurun_out/prof_trace "
                "gpurun_out/prof_fetch gpurun_out/prof_write",
 }
@@ -171,7 +185,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     os.makedirs(prof, exist_ok=True)
     lines = ["# rocprofv3 kernel statistics, %s workload (bench.py)" % workload,
              "# command: " + PROFILE_COMMANDS["trace"],
-             "# source digest of gather_plan_build_amd/csrc: " + _source_digest(),
+             "# source digest of %s: %s" % (", ".join(DIGEST_FILES), _source_digest()),
              "%-22s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
     for r in stats:
@@ -202,7 +216,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
                            "write_kib": w_copy, "fetch_scale": f_scale,
                            "write_scale": w_scale},
            "kernels": {}}
-    for k in ("k_compose_gather", "k_row_scatter"):
+    for k in ("k_compose_gather<64,1,false>", "k_row_scatter<64,1,false>"):
         if k in fetch and k in write:
             fk = sum(fetch[k]) / len(fetch[k])
             wk = sum(write[k]) / len(write[k])
@@ -212,8 +226,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
                 "read_bytes": round(1024 * fk * f_scale),
                 "write_bytes": round(1024 * wk * w_scale),
                 "hbm_bytes_per_launch": round(1024 * (fk * f_scale + wk * w_scale))}
-    if "k_compose_gather" in rec["kernels"]:
-        rec["hbm_bytes_per_launch"] = rec["kernels"]["k_compose_gather"]["hbm_bytes_per_launch"]
+    g = "k_compose_gather<64,1,false>"
+    if g in rec["kernels"]:
+        rec["hbm_bytes_per_launch"] = rec["kernels"][g]["hbm_bytes_per_launch"]
     with open(os.path.join(prof, "compose_gather_%s_counters.json" % workload), "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
@@ -299,9 +314,30 @@ def main():
                        "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": _traffic(a.workload, g_bytes),
                        "kernel": "compose_gather", "bytes_per_launch": g_bytes}
-    # layer-ahead prefetch split: the prefix gather can run a layer ahead, so
-    # the per-layer critical path is the fill (or scatter) plus the gather of
-    # the current pages only
+    if a.no_extras:
+        a.twin_index_bytes = 0
+    else:
+        _extras(a, out, runner, batch, stream, reps, L, s_ms)
+    assert int(runner.status.item()) == 0
+    if a.calibration_copy_mib:
+        n = a.calibration_copy_mib << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+    if a.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(batch, pools, curs, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def _extras(a, out, runner, batch, stream, reps, L, s_ms):
+    """Extra figures: the layer-ahead prefetch split (the prefix gather can
+    run a layer ahead, so the per-layer critical path is the fill or scatter
+    plus the gather of the current pages only), the fused fill, and the
+    index-key twin on the same plan."""
+    import gather_plan_build_amd as gpb
+    import workloads
     pre_ms = _timed(stream, lambda: [runner.gather_prefix(l, stream) for l in range(L)],
                     reps) / L
     cur_ms = _timed(stream, lambda: [runner.gather_current(l, stream) for l in range(L)],
@@ -332,17 +368,6 @@ def main():
                              "gbs": round(tb / (t_ms * 1e-3) / 1e9, 1)}
         assert int(twin.status.item()) == 0
         del ipools, icurs, twin
-    assert int(runner.status.item()) == 0
-    if a.calibration_copy_mib:
-        n = a.calibration_copy_mib << 20
-        x = torch.ones(n, dtype=torch.uint8, device="cuda")
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-    if a.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(batch, pools, curs, a.cpu_seconds)
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
