@@ -186,10 +186,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     lines = ["# rocprofv3 kernel statistics, %s workload (bench.py)" % workload,
              "# command: " + PROFILE_COMMANDS["trace"],
              "# source digest of %s: %s" % (", ".join(DIGEST_FILES), _source_digest()),
-             "%-22s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
+             "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
     for r in stats:
-        lines.append("%-22s %7s %12.0f %12.0f %12.0f %8.2f" % (
+        lines.append("%-34s %7s %12.0f %12.0f %12.0f %8.2f" % (
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]), float(r["MinNs"]),
             float(r["MaxNs"]), float(r["Percentage"])))
     with open(os.path.join(prof, "compose_%s_kernels.txt" % workload), "w") as f:
