@@ -279,6 +279,7 @@ def main():
     # the timed region: K whole steps, nothing else on the stream
     ms_per_step = _timed(stream, step, a.steps)
     assert int(runner.status.item()) == 0, "a kernel flagged a bad descriptor or row"
+    assert int(runner.plan.status.item()) == 0, "the plan kernels flagged their input"
 
     layer_bytes = runner.algorithmic_bytes_per_layer()
     value_gbs = layer_bytes * L / (ms_per_step * 1e-3) / 1e9

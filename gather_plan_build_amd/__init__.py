@@ -7,5 +7,5 @@ from .binding import (BatchMeta, GpbError, Plan, Sources, compose_gather,  # noq
                       compose_gather_slots, current_row_fill,
                       current_row_scatter, plan_build, plan_sizes, staging_clear,
                       strerror, LIB_PATH, PLAN_FIELDS, STATUS_BAD_DESCRIPTOR,
-                      STATUS_BAD_STAGING_ROW)
+                      STATUS_BAD_STAGING_ROW, STATUS_BAD_PLAN_INPUT)
 from .runner import ComposeRunner  # noqa: F401

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("GPB_LIB", os.path.join(HERE, "libgpb.so"))
 MAX_SOURCES = 64
 STATUS_BAD_DESCRIPTOR = 1
 STATUS_BAD_STAGING_ROW = 2
+STATUS_BAD_PLAN_INPUT = 4
 
 OK, EINVAL, EALIGN, EPAGE, ECAPACITY, ERANGE, EHIP = 0, -1, -2, -3, -4, -5, -6
 
@@ -42,7 +43,8 @@ PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
 
 
 class gpb_plan(ctypes.Structure):
-    _fields_ = [("d_" + f, ctypes.c_void_p) for f in PLAN_FIELDS]
+    _fields_ = [("d_" + f, ctypes.c_void_p) for f in PLAN_FIELDS] + \
+        [("d_status", ctypes.c_void_p)]
 
 
 class gpb_sources(ctypes.Structure):
@@ -204,8 +206,9 @@ class Plan:
                  "pool_locs": self.T}
         self.t = {k: torch.empty(sizes[k], dtype=torch.int32, device=dev)
                   for k in PLAN_FIELDS}
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.c = gpb_plan(*[(self.t[k].data_ptr() if sizes[k] else None)
-                            for k in PLAN_FIELDS])
+                            for k in PLAN_FIELDS], self.status.data_ptr())
 
     def build(self, stream=None):
         _check(lib.gpb_plan_build(ctypes.byref(self.meta.c), ctypes.byref(self.c),

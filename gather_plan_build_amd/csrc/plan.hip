@@ -34,7 +34,7 @@ namespace {
 constexpr int kLdsRequests = 1024;  // requests whose bases fit the LDS stage
 
 struct PlanArgs {
-  int32_t bs, ps, np, w, cap, n_pool_pages, n_slots, n_rows;
+  int32_t bs, ps, np, w, cap, n_pool_pages, n_slots, n_rows, n_cur_pages;
   const int32_t *P, *c, *req_pages;
   int32_t *slot_base, *prefix_span, *current_span;
   int32_t *q_lens, *kv_lens, *q_starts, *k_bases, *q_bases, *current_bases;
@@ -42,7 +42,16 @@ struct PlanArgs {
   int32_t *writer, *staging_rows, *mixed_locs;
   int32_t *token_req, *topk_offsets, *segments;
   int32_t *prefix_slots, *current_slots, *pool_locs;
+  int32_t *status;
 };
+
+// The kernels index by values read from the device copies of the metadata.
+// The host validated its own copies; if the device copies differ, every
+// indexed write is still kept inside its array and the fault is reported.
+__device__ __forceinline__ bool within(int x, int n) { return x >= 0 && x < n; }
+__device__ __forceinline__ void flag_bad_input(const PlanArgs &a) {
+  if (a.status) atomicOr(a.status, GPB_STATUS_BAD_PLAN_INPUT);
+}
 
 // Inclusive scan across one wave64 (Hillis-Steele over lane shuffles).
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
@@ -161,20 +170,30 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
   const int P = Pv[r];
   const int page = a.req_pages[s];
   a.slot_pages[s] = page;
+  if (!within(page, a.n_pool_pages)) {
+    flag_bad_input(a);
+    return;
+  }
   a.page_inverse[page] = s;
   const int cur_before = qb[r] / a.ps;  // current pages of earlier requests
   if (j < P) {  // prefix slot: modulo-owned pool entry, the page itself
     a.owner[s] = page % a.np;
     a.src[s] = page;
-    a.prefix_slots[s - cur_before] = s;
+    const int u = s - cur_before;
+    if (within(u, a.n_slots - a.n_cur_pages)) a.prefix_slots[u] = s;
+    else flag_bad_input(a);
   } else {      // current page i of the batch
     const int i = cur_before + (j - P);
     const int w = i % a.w;
-    a.writer[i] = w;
     a.owner[s] = a.np + w;
     a.src[s] = i + 1;
     a.staging_page_inverse[page] = w * a.cap + i + 1;
-    a.current_slots[i] = s;
+    if (within(i, a.n_cur_pages)) {
+      a.writer[i] = w;
+      a.current_slots[i] = s;
+    } else {
+      flag_bad_input(a);
+    }
   }
 }
 
@@ -202,7 +221,12 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   const int r = find_request(qs, a.bs, t);
   const int j = t - qs[r];
   const int s = base[r] + Pv[r] + j / a.ps;
-  const int loc = a.slot_pages[s] * a.ps + j % a.ps;  // the token's pool row
+  const int page = within(s, a.n_slots) ? a.slot_pages[s] : -1;
+  if (!within(page, a.n_pool_pages)) {
+    flag_bad_input(a);
+    return;
+  }
+  const int loc = page * a.ps + j % a.ps;  // the token's pool row
   const int spage = a.staging_page_inverse[loc / a.ps];
   a.staging_rows[t] = spage * a.ps + loc % a.ps;
   a.mixed_locs[t] = cb[r] + j;
@@ -281,10 +305,11 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
     if (e.n > 0 && !e.p) return GPB_EINVAL;
     if (!ok_array(e.p, e.n)) return GPB_EALIGN;
   }
+  if (o->d_status && !aligned(o->d_status, 4)) return GPB_EALIGN;
   PlanArgs a;
   a.bs = b->bs; a.ps = b->page_size; a.np = b->n_pool_entries; a.w = b->n_writers;
   a.cap = b->staging_cap_pages; a.n_pool_pages = b->n_pool_pages;
-  a.n_slots = S; a.n_rows = T;
+  a.n_slots = S; a.n_rows = T; a.n_cur_pages = NCP;
   a.P = b->d_prefix_pages; a.c = b->d_cur_tokens; a.req_pages = b->d_req_pages;
   a.slot_base = o->d_slot_base; a.prefix_span = o->d_prefix_span;
   a.current_span = o->d_current_span; a.q_lens = o->d_q_lens; a.kv_lens = o->d_kv_lens;
@@ -297,6 +322,7 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
   a.segments = o->d_segments;
   a.prefix_slots = o->d_prefix_slots; a.current_slots = o->d_current_slots;
   a.pool_locs = o->d_pool_locs;
+  a.status = o->d_status;
 
   hipStream_t st = as_stream(stream);
   // workgroup 0 scans; the rest fill the inverses (4 entries per lane-pass)

@@ -75,6 +75,10 @@ typedef enum gpb_status {
                                         >= that arena's pages; slot zeroed  */
 #define GPB_STATUS_BAD_STAGING_ROW 2 /* scatter: staging row < 0 or beyond
                                         the staging region; row skipped      */
+#define GPB_STATUS_BAD_PLAN_INPUT 4  /* plan: the device metadata differs from
+                                        the validated host copy (a page id or
+                                        index out of range); the entry is not
+                                        written                              */
 
 #define GPB_MAX_SOURCES 64           /* pointer-table entries per gather    */
 
@@ -157,6 +161,7 @@ typedef struct gpb_plan {
   int32_t *d_staging_rows, *d_mixed_locs;
   int32_t *d_token_req, *d_topk_offsets, *d_segments;
   int32_t *d_prefix_slots, *d_current_slots, *d_pool_locs;
+  int32_t *d_status;  /* optional (NULL): GPB_STATUS_* bits the kernels OR in */
 } gpb_plan;
 
 /* Pointer table of source arenas for one gather (page d63fbd4, commit

@@ -34,6 +34,7 @@ def _host(t):
 
 
 def _check_plan(batch, r, orc):
+    assert int(r.plan.status.item()) == 0, "plan kernels flagged their input"
     want = oracle.plan_for(batch, orc)
     for k in oracle.PLAN_FIELDS:
         got = _host(r.plan.t[k])
@@ -288,6 +289,38 @@ def test_sentinel_and_out_of_range_descriptors(orc):
     assert bad
     assert np.array_equal(_host(dense), want)
     assert int(status.item()) == gpb.STATUS_BAD_DESCRIPTOR
+
+
+def test_plan_reports_device_metadata_that_differs_from_the_host(orc):
+    """The host validates its own copies of the metadata; if the device copies
+    say something else (page ids out of range, a longer prefix), the plan
+    kernels keep every write inside its array and set the plan status bit.
+    A later plan from consistent copies is exact again."""
+    gpb = _gpb()
+    b = workloads.make_batch("medium")
+    meta = gpb.BatchMeta.of(b)
+    p = gpb.Plan(meta)
+    bad = p.d_req.clone()
+    bad[0] = b.n_pool_pages + 5
+    bad[7] = -3
+    p.d_req.copy_(bad)
+    p.build()
+    torch.cuda.synchronize()
+    assert int(p.status.item()) & gpb.STATUS_BAD_PLAN_INPUT
+    p.d_req.copy_(torch.from_numpy(meta.h_req).cuda())
+    p.d_prefix.copy_(p.d_prefix + 3)
+    p.status.zero_()
+    p.build()
+    torch.cuda.synchronize()
+    assert int(p.status.item()) & gpb.STATUS_BAD_PLAN_INPUT
+    p.d_prefix.copy_(torch.from_numpy(meta.h_prefix).cuda())
+    p.status.zero_()
+    p.build()
+    torch.cuda.synchronize()
+    assert int(p.status.item()) == 0
+    want = oracle.plan_for(b, orc)
+    for k in oracle.PLAN_FIELDS:
+        assert np.array_equal(_host(p.t[k]), want[k]), k
 
 
 def test_slot_list_out_of_range_is_skipped(orc):
