@@ -301,6 +301,15 @@ def main():
     g_ms = _timed(stream, lambda: [runner.gather(l, stream) for l in range(L)], reps) / L
     s_ms = _timed(stream, lambda: [runner.scatter(l, stream) for l in range(L)], reps) / L
     p_ms = _timed(stream, lambda: runner.begin_batch(stream), reps)
+    # host time of one gpb_plan_build call (validation + three launches, no
+    # synchronisation), for comparison with host-side plan builders
+    torch.cuda.synchronize()
+    n_host = 50
+    t0 = time.perf_counter()
+    for _ in range(n_host):
+        runner.plan.build(stream)
+    plan_host_us = (time.perf_counter() - t0) / n_host * 1e6
+    torch.cuda.synchronize()
     g_us, s_us = g_ms * 1e3, s_ms * 1e3
     g_bytes = runner.gather_bytes()
     achieved = g_bytes / (g_us * 1e-6) / 1e9
@@ -310,6 +319,7 @@ def main():
     out["kernels_us"] = {"compose_gather": round(g_us, 2),
                          "current_row_scatter": round(s_us, 2),
                          "plan_build_and_staging_clear": round(p_ms * 1e3, 2)}
+    out["plan_build_host_us"] = round(plan_host_us, 1)
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(achieved / HBM_PEAK_GBS, 4),

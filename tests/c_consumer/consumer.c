@@ -1,0 +1,193 @@
+/*
+ * A plain C consumer of include/gpb.h: no torch, no C++.  Device memory comes
+ * from the HIP runtime API directly.
+ *
+ *   consumer check            host-only: error paths and plan sizes
+ *   consumer run <in> <out>   read a batch (binary, see below), build the plan,
+ *                             clear staging, scatter and gather one layer on
+ *                             the GPU, write the plan arrays, staging and
+ *                             dense buffer to <out>
+ *
+ * Input file (int32 little endian unless noted): bs, page_size, row_bytes,
+ * n_pool_pages, n_pool_entries, n_writers, staging_cap_pages, then P[bs],
+ * c[bs], n_req, req_pages[n_req], then the pool bytes
+ * (n_pool_pages*page_size*row_bytes) and the current rows (T*row_bytes).
+ * Output: S, T, NCP, the plan arrays in the header's order, staging bytes,
+ * dense bytes.
+ */
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "gpb.h"
+
+#define CHECK(x) do { int rc_ = (x); if (rc_ != GPB_OK) { \
+  fprintf(stderr, "%s:%d %s -> %d (%s)\n", __FILE__, __LINE__, #x, rc_, gpb_strerror(rc_)); \
+  return 2; } } while (0)
+#define HCHECK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { \
+  fprintf(stderr, "%s:%d %s -> %s\n", __FILE__, __LINE__, #x, hipGetErrorString(e_)); \
+  return 3; } } while (0)
+
+static int expect(int got, int want, const char *what) {
+  if (got != want) {
+    fprintf(stderr, "%s: got %d want %d\n", what, got, want);
+    return 1;
+  }
+  return 0;
+}
+
+static int check(void) {
+  int32_t P[2] = {3, 5}, c[2] = {100, 37};
+  int32_t pages[11] = {10, 20, 30, 40, 50, 60, 70, 80, 90, 100, 110};
+  gpb_batch b;
+  memset(&b, 0, sizeof b);
+  b.bs = 2; b.page_size = 64; b.row_bytes = 1152; b.n_pool_pages = 256;
+  b.n_pool_entries = 1; b.n_writers = 1; b.staging_cap_pages = 6;
+  b.h_prefix_pages = P; b.h_cur_tokens = c; b.h_req_pages = pages;
+  int32_t S = -1, T = -1, NCP = -1;
+  int bad = 0;
+  bad |= expect(gpb_plan_sizes(&b, &S, &T, &NCP), GPB_OK, "sizes");
+  bad |= expect(S, 11, "S") | expect(T, 137, "T") | expect(NCP, 3, "NCP");
+  pages[4] = 0;
+  bad |= expect(gpb_plan_sizes(&b, NULL, NULL, NULL), GPB_EPAGE, "dummy page");
+  pages[4] = 50;
+  b.staging_cap_pages = 3;
+  bad |= expect(gpb_plan_sizes(&b, NULL, NULL, NULL), GPB_ECAPACITY, "capacity");
+  b.staging_cap_pages = 6;
+  b.row_bytes = 1000;
+  bad |= expect(gpb_plan_sizes(&b, NULL, NULL, NULL), GPB_EALIGN, "row bytes");
+  b.row_bytes = 1152;
+  gpb_plan p;
+  memset(&p, 0, sizeof p);
+  bad |= expect(gpb_plan_build(&b, &p, NULL), GPB_EINVAL, "plan without outputs");
+  gpb_sources t;
+  memset(&t, 0, sizeof t);
+  bad |= expect(gpb_compose_gather(NULL, &t, NULL, NULL, 4, 64, 1152, NULL, NULL),
+                GPB_EINVAL, "empty table");
+  bad |= expect(gpb_current_row_scatter(NULL, 8, NULL, NULL, 0, 1152, NULL, NULL),
+                GPB_OK, "empty scatter");
+  bad |= expect(gpb_staging_clear(NULL, 0, NULL), GPB_OK, "empty clear");
+  if (!bad) printf("c consumer: host checks ok\n");
+  return bad;
+}
+
+static int32_t rd32(FILE *f) {
+  int32_t v = 0;
+  if (fread(&v, 4, 1, f) != 1) { fprintf(stderr, "short input\n"); exit(4); }
+  return v;
+}
+
+static int run(const char *in, const char *out) {
+  FILE *f = fopen(in, "rb");
+  if (!f) return 4;
+  gpb_batch b;
+  memset(&b, 0, sizeof b);
+  b.bs = rd32(f); b.page_size = rd32(f); b.row_bytes = rd32(f);
+  b.n_pool_pages = rd32(f); b.n_pool_entries = rd32(f); b.n_writers = rd32(f);
+  b.staging_cap_pages = rd32(f);
+  int32_t *P = calloc((size_t)b.bs + 1, 4), *c = calloc((size_t)b.bs + 1, 4);
+  for (int r = 0; r < b.bs; r++) P[r] = rd32(f);
+  for (int r = 0; r < b.bs; r++) c[r] = rd32(f);
+  int32_t n_req = rd32(f);
+  int32_t *req = calloc((size_t)n_req + 1, 4);
+  for (int k = 0; k < n_req; k++) req[k] = rd32(f);
+  b.h_prefix_pages = P; b.h_cur_tokens = c; b.h_req_pages = req;
+  int32_t S, T, NCP;
+  CHECK(gpb_plan_sizes(&b, &S, &T, &NCP));
+  const size_t RB = (size_t)b.row_bytes, PS = (size_t)b.page_size;
+  const size_t pool_bytes = (size_t)b.n_pool_pages * PS * RB;
+  const size_t cur_bytes = (size_t)T * RB;
+  const size_t stag_rows = (size_t)b.n_writers * b.staging_cap_pages * PS;
+  uint8_t *h_pool = malloc(pool_bytes), *h_cur = malloc(cur_bytes + 1);
+  if (fread(h_pool, 1, pool_bytes, f) != pool_bytes) return 4;
+  if (cur_bytes && fread(h_cur, 1, cur_bytes, f) != cur_bytes) return 4;
+  fclose(f);
+
+  /* device copies of the metadata, the arenas and every plan output */
+  void *d_P, *d_c, *d_req, *d_pool, *d_cur, *d_stag, *d_dense, *d_status;
+  HCHECK(hipMalloc(&d_P, 4 * (size_t)b.bs + 4));
+  HCHECK(hipMalloc(&d_c, 4 * (size_t)b.bs + 4));
+  HCHECK(hipMalloc(&d_req, 4 * (size_t)n_req + 4));
+  HCHECK(hipMalloc(&d_pool, pool_bytes));
+  HCHECK(hipMalloc(&d_cur, cur_bytes + 16));
+  HCHECK(hipMalloc(&d_stag, stag_rows * RB));
+  HCHECK(hipMalloc(&d_dense, (size_t)S * PS * RB + 16));
+  HCHECK(hipMalloc(&d_status, 4));
+  HCHECK(hipMemcpy(d_P, P, 4 * (size_t)b.bs, hipMemcpyHostToDevice));
+  HCHECK(hipMemcpy(d_c, c, 4 * (size_t)b.bs, hipMemcpyHostToDevice));
+  HCHECK(hipMemcpy(d_req, req, 4 * (size_t)n_req, hipMemcpyHostToDevice));
+  HCHECK(hipMemcpy(d_pool, h_pool, pool_bytes, hipMemcpyHostToDevice));
+  if (cur_bytes) HCHECK(hipMemcpy(d_cur, h_cur, cur_bytes, hipMemcpyHostToDevice));
+  HCHECK(hipMemset(d_status, 0, 4));
+  b.d_prefix_pages = d_P; b.d_cur_tokens = d_c; b.d_req_pages = d_req;
+
+  /* plan outputs in the header's order, with their sizes */
+  const int64_t bs = b.bs, npp = b.n_pool_pages;
+  const int64_t sizes[] = {bs, 2 * bs, 2 * bs, bs, bs, bs, bs, bs, bs, S, S, S, npp, npp,
+                           NCP, T, T, T, T, 4 * bs, S - NCP, NCP, T};
+  enum { NF = sizeof sizes / sizeof sizes[0] };
+  int32_t *outs[NF];
+  for (int k = 0; k < NF; k++) HCHECK(hipMalloc((void **)&outs[k], 4 * (size_t)sizes[k] + 4));
+  gpb_plan p;
+  int32_t **fields[NF] = {&p.d_slot_base, &p.d_prefix_span, &p.d_current_span, &p.d_q_lens,
+                          &p.d_kv_lens, &p.d_q_starts, &p.d_k_bases, &p.d_q_bases,
+                          &p.d_current_bases, &p.d_slot_pages, &p.d_owner, &p.d_src,
+                          &p.d_page_inverse, &p.d_staging_page_inverse, &p.d_writer,
+                          &p.d_staging_rows, &p.d_mixed_locs, &p.d_token_req,
+                          &p.d_topk_offsets, &p.d_segments, &p.d_prefix_slots,
+                          &p.d_current_slots, &p.d_pool_locs};
+  for (int k = 0; k < NF; k++) *fields[k] = outs[k];
+  p.d_status = d_status;
+
+  hipStream_t st;
+  HCHECK(hipStreamCreate(&st));
+  CHECK(gpb_plan_build(&b, &p, st));
+  CHECK(gpb_staging_clear(d_stag, (int64_t)(stag_rows * RB), st));
+  CHECK(gpb_current_row_scatter(d_stag, (int64_t)stag_rows, p.d_staging_rows, d_cur, T,
+                                b.row_bytes, d_status, st));
+  gpb_sources t;
+  memset(&t, 0, sizeof t);
+  t.n = b.n_pool_entries + b.n_writers;
+  for (int e = 0; e < b.n_pool_entries; e++) {
+    t.base[e] = d_pool;
+    t.n_pages[e] = b.n_pool_pages;
+  }
+  for (int w = 0; w < b.n_writers; w++) {
+    t.base[b.n_pool_entries + w] = (uint8_t *)d_stag + (size_t)w * b.staging_cap_pages * PS * RB;
+    t.n_pages[b.n_pool_entries + w] = b.staging_cap_pages;
+  }
+  CHECK(gpb_compose_gather(d_dense, &t, p.d_owner, p.d_src, S, b.page_size, b.row_bytes,
+                           d_status, st));
+  HCHECK(hipStreamSynchronize(st));
+  int32_t status = -1;
+  HCHECK(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+  if (status != 0) { fprintf(stderr, "status %d\n", status); return 5; }
+
+  FILE *o = fopen(out, "wb");
+  if (!o) return 4;
+  int32_t head[3] = {S, T, NCP};
+  fwrite(head, 4, 3, o);
+  for (int k = 0; k < NF; k++) {
+    int32_t *h = malloc(4 * (size_t)sizes[k] + 4);
+    HCHECK(hipMemcpy(h, outs[k], 4 * (size_t)sizes[k], hipMemcpyDeviceToHost));
+    fwrite(h, 4, (size_t)sizes[k], o);
+    free(h);
+  }
+  uint8_t *h = malloc(stag_rows * RB + (size_t)S * PS * RB + 1);
+  HCHECK(hipMemcpy(h, d_stag, stag_rows * RB, hipMemcpyDeviceToHost));
+  fwrite(h, 1, stag_rows * RB, o);
+  if (S) HCHECK(hipMemcpy(h, d_dense, (size_t)S * PS * RB, hipMemcpyDeviceToHost));
+  fwrite(h, 1, (size_t)S * PS * RB, o);
+  fclose(o);
+  printf("c consumer: ran S=%d T=%d NCP=%d\n", S, T, NCP);
+  return 0;
+}
+
+int main(int argc, char **argv) {
+  if (argc >= 2 && strcmp(argv[1], "check") == 0) return check();
+  if (argc >= 4 && strcmp(argv[1], "run") == 0) return run(argv[2], argv[3]);
+  fprintf(stderr, "usage: consumer check | consumer run <in> <out>\n");
+  return 1;
+}
