@@ -71,7 +71,7 @@ def _source_digest():
     return h.hexdigest()[:16]
 
 
-def _traffic(workload, gather_launch_bytes):
+def _traffic(workload):
     """HBM bytes per gather launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "compose_gather_%s_counters.json" % workload)
@@ -323,7 +323,7 @@ def main():
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(achieved / HBM_PEAK_GBS, 4),
-                       "traffic": _traffic(a.workload, g_bytes),
+                       "traffic": _traffic(a.workload),
                        "kernel": "compose_gather", "bytes_per_launch": g_bytes}
     if a.no_extras:
         a.twin_index_bytes = 0

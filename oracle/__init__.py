@@ -38,7 +38,6 @@ Parity status per function (pins in tests/test_oracle_pins.py):
   "parity unpinned" as far as the pages themselves go.
 """
 import ctypes
-import os
 
 import numpy as np
 
@@ -275,7 +274,3 @@ def layer_for(batch, plan_arrays, pool, cur, staging, orc=None):
     return o.compose_layer(table, cur, plan_arrays["staging_rows"],
                            plan_arrays["owner"], plan_arrays["src"],
                            batch.page_size, batch.row_bytes, staging)
-
-
-def lib_dir():
-    return os.path.dirname(os.path.abspath(__file__))

@@ -14,7 +14,7 @@ measure (page d63fbd4, commit "cut per-layer CPU on the prefill launch
 path": bs=12 with 44.6K current tokens; 78-layer forward; 64-token pages of
 576-wide rows).  That trace is not available, so its shape is drawn here.
 """
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import numpy as np
 import torch
@@ -48,7 +48,6 @@ class Batch:
     n_rotations: int = 1          # distinct pool/current arenas cycled per layer
     value_kind: str = "bf16_normal"   # or "bytes"
     seed: int = 0
-    notes: dict = field(default_factory=dict)
 
     @property
     def n_req_pages(self):
