@@ -60,6 +60,7 @@ def _args():
 # include from the library (plan kernels and host entry points elsewhere do
 # not change the gather's traffic)
 DIGEST_FILES = ("gather_plan_build_amd/csrc/compose.hip",
+                "gather_plan_build_amd/csrc/buffer_io.h",
                 "gather_plan_build_amd/csrc/gpb_common.h")
 
 
@@ -328,7 +329,7 @@ def main():
     if a.no_extras:
         a.twin_index_bytes = 0
     else:
-        _extras(a, out, runner, batch, stream, reps, L, s_ms)
+        _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms)
     assert int(runner.status.item()) == 0
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib << 20
@@ -342,7 +343,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _extras(a, out, runner, batch, stream, reps, L, s_ms):
+def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
     """Extra figures: the layer-ahead prefetch split (the prefix gather can
     run a layer ahead, so the per-layer critical path is the fill or scatter
     plus the gather of the current pages only), the fused fill, and the
@@ -374,9 +375,15 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms):
         twin.begin_batch(stream)
         t_ms = _timed(stream, lambda: [twin.layer(l, stream) for l in range(L)], reps) / L
         tb = twin.algorithmic_bytes_per_layer()
+        both_ms = _timed(stream, lambda: [gpb.layer_groups([runner, twin], l, stream)
+                                          for l in range(L)], reps) / L
+        both_b = runner.algorithmic_bytes_per_layer() + tb
         out["index_twin"] = {"row_bytes": rb, "us_per_layer": round(t_ms * 1e3, 2),
                              "algorithmic_bytes_per_layer": tb,
-                             "gbs": round(tb / (t_ms * 1e-3) / 1e9, 1)}
+                             "gbs": round(tb / (t_ms * 1e-3) / 1e9, 1),
+                             "token_and_twin_separate_us": round((s_ms + g_ms + t_ms) * 1e3, 2),
+                             "token_and_twin_grouped_us": round(both_ms * 1e3, 2),
+                             "grouped_gbs": round(both_b / (both_ms * 1e-3) / 1e9, 1)}
         assert int(twin.status.item()) == 0
         del ipools, icurs, twin
 

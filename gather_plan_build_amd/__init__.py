@@ -5,7 +5,8 @@ Importing this package loads libgpb.so and fails loudly if it is missing.
 """
 from .binding import (BatchMeta, GpbError, Plan, Sources, compose_gather,  # noqa: F401
                       compose_gather_slots, current_row_fill,
+                      compose_gather_groups, current_row_scatter_groups,
                       current_row_scatter, plan_build, plan_sizes, staging_clear,
                       strerror, LIB_PATH, PLAN_FIELDS, STATUS_BAD_DESCRIPTOR,
                       STATUS_BAD_STAGING_ROW, STATUS_BAD_PLAN_INPUT)
-from .runner import ComposeRunner  # noqa: F401
+from .runner import ComposeRunner, layer_groups  # noqa: F401

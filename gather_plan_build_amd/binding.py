@@ -53,6 +53,20 @@ class gpb_sources(ctypes.Structure):
                 ("n_pages", ctypes.c_int64 * MAX_SOURCES)]
 
 
+MAX_GROUPS = 4
+MAX_GROUP_SOURCES = 16
+
+
+class gpb_row_group(ctypes.Structure):
+    _fields_ = [("d_staging", ctypes.c_void_p), ("n_staging_rows", ctypes.c_int64),
+                ("d_cur_rows", ctypes.c_void_p), ("row_bytes", ctypes.c_int32)]
+
+
+class gpb_gather_group(ctypes.Structure):
+    _fields_ = [("d_dense", ctypes.c_void_p), ("table", ctypes.POINTER(gpb_sources)),
+                ("row_bytes", ctypes.c_int32)]
+
+
 def _hip_runtimes():
     """Distinct libamdhip64 files mapped into this process."""
     found = set()
@@ -91,11 +105,16 @@ def _load(path):
     lib.gpb_compose_gather_slots.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, i32, vp,
                                              vp, i32, i32, i32, vp, vp]
     lib.gpb_current_row_fill.argtypes = [vp, i64, vp, vp, i64, vp, vp, i32, i32, vp, vp]
+    lib.gpb_current_row_scatter_groups.argtypes = [ctypes.POINTER(gpb_row_group), i32, vp,
+                                                   i32, vp, vp]
+    lib.gpb_compose_gather_groups.argtypes = [ctypes.POINTER(gpb_gather_group), i32, vp, vp,
+                                              i32, i32, vp, vp]
     lib.gpb_strerror.argtypes = [ctypes.c_int]
     lib.gpb_strerror.restype = ctypes.c_char_p
     for f in ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
               "gpb_current_row_scatter", "gpb_compose_gather",
-              "gpb_compose_gather_slots", "gpb_current_row_fill"):
+              "gpb_compose_gather_slots", "gpb_current_row_fill",
+              "gpb_current_row_scatter_groups", "gpb_compose_gather_groups"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -104,7 +123,8 @@ lib = _load(LIB_PATH)
 
 EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
            "gpb_current_row_scatter", "gpb_compose_gather", "gpb_compose_gather_slots",
-           "gpb_current_row_fill", "gpb_strerror")
+           "gpb_current_row_fill", "gpb_current_row_scatter_groups",
+           "gpb_compose_gather_groups", "gpb_strerror")
 
 
 class GpbError(RuntimeError):
@@ -282,3 +302,25 @@ def current_row_fill(staging, n_staging_rows, staging_rows, pool, n_pool_rows, p
                                     _ptr(cur_rows), int(n_rows), int(row_bytes),
                                     _ptr(status), _stream(stream)),
            "gpb_current_row_fill")
+
+
+def current_row_scatter_groups(groups, staging_rows, n_rows, status=None, stream=None):
+    """One launch scattering the current rows of every group:
+    groups = [(staging, n_staging_rows, cur_rows, row_bytes), ...]."""
+    arr = (gpb_row_group * max(len(groups), 1))(
+        *[gpb_row_group(_ptr(st), int(n), _ptr(cur), int(rb)) for st, n, cur, rb in groups])
+    _check(lib.gpb_current_row_scatter_groups(arr, len(groups), _ptr(staging_rows),
+                                              int(n_rows), _ptr(status), _stream(stream)),
+           "gpb_current_row_scatter_groups")
+
+
+def compose_gather_groups(groups, owner, src, n_slots, page_rows, status=None, stream=None):
+    """One launch gathering every group: groups = [(dense, Sources, row_bytes), ...]."""
+    keep = [g[1] if isinstance(g[1], Sources) else Sources(g[1]) for g in groups]
+    arr = (gpb_gather_group * max(len(groups), 1))(
+        *[gpb_gather_group(_ptr(d), ctypes.pointer(t.c), int(rb))
+          for (d, _, rb), t in zip(groups, keep)])
+    _check(lib.gpb_compose_gather_groups(arr, len(groups), _ptr(owner), _ptr(src),
+                                         int(n_slots), int(page_rows), _ptr(status),
+                                         _stream(stream)),
+           "gpb_compose_gather_groups")

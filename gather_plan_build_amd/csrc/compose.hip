@@ -27,6 +27,7 @@
 #include <algorithm>
 #include <cstdio>
 
+#include "buffer_io.h"
 #include "gpb_common.h"
 
 #ifndef GPB_GATHER_BLOCK
@@ -41,12 +42,6 @@
 #ifndef GPB_SCATTER_CPT
 #define GPB_SCATTER_CPT 1      // 16-byte chunks per lane
 #endif
-#ifndef GPB_LOAD_POLICY
-#define GPB_LOAD_POLICY 2      // cache-policy bits of the buffer loads (nt)
-#endif
-#ifndef GPB_STORE_POLICY
-#define GPB_STORE_POLICY 2     // cache-policy bits of the buffer stores (nt)
-#endif
 
 namespace gpb {
 namespace {
@@ -56,24 +51,6 @@ struct SrcTable {
   int64_t n_pages[GPB_MAX_SOURCES];
   int32_t n;
 };
-
-// Raw buffer resources: a base address plus a byte range the hardware checks
-// on every access.  A load outside the range returns zeros and a store
-// outside it is dropped, so ragged tails, -1 sentinels and bad rows need no
-// branches around the memory instructions (branches around them would make
-// the compiler wait for each store before the next).
-constexpr int kRsrcWord3 = 0x00020000;         // 32-bit data format, raw addressing
-constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every range we build
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kRsrcWord3);
-}
-__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, GPB_LOAD_POLICY);
-}
-__device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, GPB_STORE_POLICY);
-}
 
 // One workgroup per unit of a slot's page, units of a page consecutive.  The
 // slot's descriptor is uniform across the workgroup: owner/src are scalar

@@ -163,3 +163,20 @@ class ComposeRunner:
 
     def scatter_bytes(self):
         return 2 * self.T * self.rb + 4 * self.T
+
+
+def layer_groups(runners, layer, stream=None):
+    """One layer for several row formats sharing one plan (the token KV and
+    its index-key twin): one scatter launch and one gather launch for all of
+    them."""
+    r0 = runners[0]
+    for r in runners[1:]:
+        assert r.plan is r0.plan
+    h = layer % PARITY
+    t = r0.plan.t
+    B.current_row_scatter_groups(
+        [(r.staging[h], r.staging_rows_total, r.curs[layer % len(r.curs)], r.rb)
+         for r in runners], t["staging_rows"], r0.T, r0.status, stream)
+    B.compose_gather_groups(
+        [(r.dense[h], r.tables[(layer % len(r.pools), h)], r.rb) for r in runners],
+        t["owner"], t["src"], r0.S, r0.ps, r0.status, stream)

@@ -255,6 +255,41 @@ int gpb_current_row_fill(void *d_staging, int64_t n_staging_rows,
                          const void *d_cur_rows, int32_t n_rows, int32_t row_bytes,
                          int32_t *d_status, void *stream);
 
+/* Several row formats composed on one plan in one launch each (page 0d87bc5,
+ * commit "prefetch staging exchange": the indexer-key fill reuses the token
+ * plan's staging page inverse; the index twin of the compose runs beside the
+ * token-KV compose).  Every group has its own arenas and row size and shares
+ * the plan's staging_rows / owner / src; the result is the one the
+ * single-format calls give per group.  Up to GPB_MAX_GROUPS groups; a group's
+ * table holds at most GPB_MAX_GROUP_SOURCES entries. */
+#define GPB_MAX_GROUPS 4
+#define GPB_MAX_GROUP_SOURCES 16
+
+typedef struct gpb_row_group {      /* one format's current-row scatter */
+  void *d_staging;                  /* n_staging_rows rows of row_bytes  */
+  int64_t n_staging_rows;
+  const void *d_cur_rows;           /* n_rows rows of row_bytes           */
+  int32_t row_bytes;                /* multiple of 16                     */
+} gpb_row_group;
+
+typedef struct gpb_gather_group {   /* one format's slot-dense gather      */
+  void *d_dense;                    /* n_slots pages of page_rows*row_bytes */
+  const gpb_sources *table;         /* n <= GPB_MAX_GROUP_SOURCES          */
+  int32_t row_bytes;                /* multiple of 16                     */
+} gpb_gather_group;
+
+/* gpb_current_row_scatter for every group, one launch. */
+int gpb_current_row_scatter_groups(const gpb_row_group *groups, int32_t n_groups,
+                                   const int32_t *d_staging_rows, int32_t n_rows,
+                                   int32_t *d_status, void *stream);
+
+/* gpb_compose_gather for every group (same descriptors and page_rows), one
+ * launch. */
+int gpb_compose_gather_groups(const gpb_gather_group *groups, int32_t n_groups,
+                              const int32_t *d_owner, const int32_t *d_src,
+                              int32_t n_slots, int32_t page_rows, int32_t *d_status,
+                              void *stream);
+
 /* Static, human-readable name of a gpb_status value. */
 const char *gpb_strerror(int status);
 

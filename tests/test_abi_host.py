@@ -149,6 +149,40 @@ def test_slot_gather_and_fill_argument_checks():
     assert f(a, 10, a, a, 100, a, a, 4, 1000, None, None) == B.EALIGN
 
 
+def test_group_argument_checks():
+    a = 0x100000
+    t = B.Sources([(a, 10), (a, 4)])
+    big = B.Sources([(a, 1)] * 17)
+
+    def gg(*groups):
+        return (B.gpb_gather_group * len(groups))(*groups)
+
+    def rg(*groups):
+        return (B.gpb_row_group * len(groups))(*groups)
+
+    G = B.lib.gpb_compose_gather_groups
+    ok = gg(B.gpb_gather_group(a, ctypes.pointer(t.c), 1152),
+            B.gpb_gather_group(a, ctypes.pointer(t.c), 144))
+    assert G(ok, 2, a, a, 0, 64, None, None) == B.OK          # no slots: no launch
+    assert G(ok, 0, a, a, 4, 64, None, None) == B.EINVAL
+    assert G(ok, 5, a, a, 4, 64, None, None) == B.EINVAL
+    assert G(gg(B.gpb_gather_group(a, ctypes.pointer(big.c), 1152)), 1, a, a, 4, 64,
+             None, None) == B.EINVAL                           # > 16 table entries
+    assert G(gg(B.gpb_gather_group(a, ctypes.pointer(t.c), 1000)), 1, a, a, 4, 64,
+             None, None) == B.EALIGN
+    assert G(gg(B.gpb_gather_group(a + 8, ctypes.pointer(t.c), 1152)), 1, a, a, 4, 64,
+             None, None) == B.EALIGN
+    assert G(ok, 2, None, a, 4, 64, None, None) == B.EINVAL
+    S = B.lib.gpb_current_row_scatter_groups
+    rok = rg(B.gpb_row_group(a, 10, a, 1152), B.gpb_row_group(a, 10, a, 144))
+    assert S(rok, 2, a, 0, None, None) == B.OK
+    assert S(rok, 2, None, 4, None, None) == B.EINVAL
+    assert S(rok, 0, a, 4, None, None) == B.EINVAL
+    assert S(rg(B.gpb_row_group(a, 10, a, 100)), 1, a, 4, None, None) == B.EALIGN
+    assert S(rg(B.gpb_row_group(a + 4, 10, a, 144)), 1, a, 4, None, None) == B.EALIGN
+    assert S(rg(B.gpb_row_group(a, 1 << 40, a, 144)), 1, a, 4, None, None) == B.ERANGE
+
+
 def test_staging_clear_argument_checks():
     f = B.lib.gpb_staging_clear
     assert f(0x100000, 0, None) == B.OK

@@ -443,3 +443,67 @@ def test_batch_replays_in_a_hip_graph(orc):
             assert np.array_equal(_host(r.plan.t[k]), want[k]), (rep, k)
         _say("  replay", rep, "ok")
     assert _status(r) == 0
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_grouped_formats_match_single_format(orc, seed):
+    """One scatter launch and one gather launch for two or three row formats
+    on one plan give, per format, the single-format result (the oracle's)."""
+    gpb = _gpb()
+    rng = np.random.default_rng(900 + seed)
+    for i in range(12):
+        b = workloads.random_batch(rng, page_size=int(rng.choice([1, 4, 16, 64])))
+        sizes = [b.row_bytes] + [int(16 * rng.integers(1, 10))
+                                 for _ in range(int(rng.integers(1, 3)))]
+        runners, host = [], []
+        plan = None
+        for k, rb in enumerate(sizes):
+            bk = workloads.Batch(b.name, b.bs, b.page_size, rb, b.n_pool_pages,
+                                 b.n_pool_entries, b.n_writers, b.staging_cap_pages,
+                                 b.prefix_pages, b.cur_tokens, b.req_pages)
+            pool_np, cur_np = pins.tagged_values(bk, seed=seed * 100 + i * 10 + k)
+            meta = gpb.BatchMeta.of(bk)
+            r = gpb.ComposeRunner(meta, [torch.from_numpy(pool_np).cuda()],
+                                  [torch.from_numpy(cur_np).cuda()], plan=plan)
+            plan = r.plan
+            runners.append(r)
+            host.append((bk, pool_np, cur_np))
+        for r in runners:
+            r.begin_batch()
+        for layer in range(2):
+            gpb.layer_groups(runners, layer)
+        torch.cuda.synchronize()
+        want = _check_plan(host[0][0], runners[0], orc)
+        for r, (bk, pool_np, cur_np) in zip(runners, host):
+            for layer in range(2):
+                _check_layer(bk, r, layer, want, [pool_np], [cur_np], orc)
+            assert _status(r) == 0
+    _say("grouped seed", seed, "ok")
+
+
+def test_token_and_index_twin_in_one_launch_each(orc):
+    """The traced batch's token KV (1152-byte rows) and index keys (144-byte
+    rows) composed with grouped launches, four layers, byte-exact."""
+    gpb = _gpb()
+    b = workloads.make_batch("traced")
+    rb = workloads.INDEX_ROW_BYTES
+    pools, curs = workloads.make_values(b, device="cuda", rotations=2)
+    tok = _runner(b, pools, curs)
+    ipools, icurs = workloads.make_values(b, device="cuda", rotations=2, row_bytes=rb,
+                                          value_kind="bytes", seed=1)
+    bi = workloads.Batch(b.name, b.bs, b.page_size, rb, b.n_pool_pages, b.n_pool_entries,
+                         b.n_writers, b.staging_cap_pages, b.prefix_pages, b.cur_tokens,
+                         b.req_pages)
+    twin = gpb.ComposeRunner(gpb.BatchMeta.of(bi), ipools, icurs, plan=tok.plan)
+    tok.begin_batch()
+    twin.begin_batch()
+    want = _check_plan(b, tok, orc)
+    pools_np, curs_np = [_host(p) for p in pools], [_host(c) for c in curs]
+    ipools_np, icurs_np = [_host(p) for p in ipools], [_host(c) for c in icurs]
+    for layer in range(4):
+        gpb.layer_groups([tok, twin], layer)
+        torch.cuda.synchronize()
+        _check_layer(b, tok, layer, want, pools_np, curs_np, orc)
+        _check_layer(bi, twin, layer, want, ipools_np, icurs_np, orc)
+        _say("  grouped layer", layer, "ok")
+    assert _status(tok) == 0 and _status(twin) == 0
