@@ -83,8 +83,8 @@ def _hip_runtimes():
 
 def _load(path):
     if not os.path.exists(path):
-        raise ImportError("libgpb.so not built at %s: run python -m "
-                          "gather_plan_build_amd.build (no fallback exists)" % path)
+        raise ImportError("libgpb.so not built at %s: run python "
+                          "gather_plan_build_amd/build.py (no fallback exists)" % path)
     # torch provides device memory and streams; its HIP runtime must be the
     # one libgpb.so binds to (same SONAME, loaded first), or the process would
     # hold two runtimes whose streams and devices do not mix.

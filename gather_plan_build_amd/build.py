@@ -1,6 +1,8 @@
 """Build libgpb.so in-tree with hipcc for gfx950.
 
-    python -m gather_plan_build_amd.build [--define NAME=VALUE ...] [--out PATH]
+    python gather_plan_build_amd/build.py [--define NAME=VALUE ...] [--out PATH]
+
+(run as a script: importing the package needs the library this builds)
 
 Every HIP source under csrc/ goes into one shared library next to this file.
 Packed-FP32 instructions are switched off for all device code.
