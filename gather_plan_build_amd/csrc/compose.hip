@@ -18,8 +18,8 @@
 //     default), walked in address order: on MI355X this measured faster than
 //     fewer, larger units (more chunks in flight per lane, 256-lane
 //     workgroups), than part-major orders and than XCD-blocked orders;
-//   - loads and stores are non-temporal: each byte is read once and written
-//     once per layer;
+//   - loads are non-temporal (each byte is read once per layer); stores carry
+//     the sc1 policy bit, measured faster than non-temporal stores here;
 //   - raw buffer resources bound every access, so ragged tails, -1 sentinels
 //     and bad rows cost no branches.
 // The unit shape and cache-policy bits can be overridden at build time
