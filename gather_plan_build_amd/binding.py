@@ -39,7 +39,8 @@ PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
                "q_starts", "k_bases", "q_bases", "current_bases", "slot_pages",
                "owner", "src", "page_inverse", "staging_page_inverse", "writer",
                "staging_rows", "mixed_locs", "token_req", "topk_offsets", "segments",
-               "prefix_slots", "current_slots", "pool_locs")
+               "prefix_slots", "current_slots", "pool_locs", "cur_page_token0",
+               "cur_page_ntok")
 
 
 class gpb_plan(ctypes.Structure):
@@ -223,7 +224,8 @@ class Plan:
                  "staging_rows": self.T, "mixed_locs": self.T, "token_req": self.T,
                  "topk_offsets": self.T, "segments": 4 * bs,
                  "prefix_slots": self.S - self.NCP, "current_slots": self.NCP,
-                 "pool_locs": self.T}
+                 "pool_locs": self.T, "cur_page_token0": self.NCP,
+                 "cur_page_ntok": self.NCP}
         self.t = {k: torch.empty(sizes[k], dtype=torch.int32, device=dev)
                   for k in PLAN_FIELDS}
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -324,3 +326,4 @@ def compose_gather_groups(groups, owner, src, n_slots, page_rows, status=None, s
                                          int(n_slots), int(page_rows), _ptr(status),
                                          _stream(stream)),
            "gpb_compose_gather_groups")
+

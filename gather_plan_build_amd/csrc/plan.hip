@@ -16,8 +16,8 @@
 //      spans and ragged descriptors; the other workgroups fill both page
 //      inverses with -1.
 //   2. k_plan_slots: one lane per dense slot -> slot page, page inverse,
-//      gather descriptor, writer, staging page inverse, and the slot's place
-//      in the prefix or current slot list.
+//      gather descriptor, writer, staging page inverse, the slot's place in
+//      the prefix or current slot list, and a current page's token range.
 //   3. k_plan_tokens: one lane per current token -> staging row through the
 //      staging page inverse, mixed_locs, the per-token expansions (request
 //      row id, top-k offset) and the token's pool row.
@@ -42,6 +42,7 @@ struct PlanArgs {
   int32_t *writer, *staging_rows, *mixed_locs;
   int32_t *token_req, *topk_offsets, *segments;
   int32_t *prefix_slots, *current_slots, *pool_locs;
+  int32_t *cur_page_token0, *cur_page_ntok;
   int32_t *status;
 };
 
@@ -150,19 +151,24 @@ __device__ __forceinline__ int find_request(const int32_t *base, int bs, int x) 
 }
 
 __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
-  __shared__ int32_t s_base[kLdsRequests], s_P[kLdsRequests], s_qb[kLdsRequests];
+  __shared__ int32_t s_base[kLdsRequests], s_P[kLdsRequests], s_qb[kLdsRequests],
+      s_qs[kLdsRequests], s_c[kLdsRequests];
   const bool lds = a.bs <= kLdsRequests;
   if (lds) {
     for (int r = threadIdx.x; r < a.bs; r += kBlock) {
       s_base[r] = a.slot_base[r];
       s_P[r] = a.P[r];
       s_qb[r] = a.q_bases[r];
+      s_qs[r] = a.q_starts[r];
+      s_c[r] = a.c[r];
     }
     __syncthreads();
   }
   const int32_t *base = lds ? s_base : a.slot_base;
   const int32_t *Pv = lds ? s_P : a.P;
   const int32_t *qb = lds ? s_qb : a.q_bases;
+  const int32_t *qs = lds ? s_qs : a.q_starts;
+  const int32_t *cv = lds ? s_c : a.c;
   const int s = blockIdx.x * kBlock + threadIdx.x;
   if (s >= a.n_slots) return;
   const int r = find_request(base, a.bs, s);
@@ -189,8 +195,11 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
     a.src[s] = i + 1;
     a.staging_page_inverse[page] = w * a.cap + i + 1;
     if (within(i, a.n_cur_pages)) {
+      const int k = j - P;  // page k of the request's current pages
       a.writer[i] = w;
       a.current_slots[i] = s;
+      a.cur_page_token0[i] = qs[r] + k * a.ps;
+      a.cur_page_ntok[i] = min(a.ps, cv[r] - k * a.ps);
     } else {
       flag_bad_input(a);
     }
@@ -300,7 +309,8 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
       {o->d_page_inverse, npp}, {o->d_staging_page_inverse, npp},
       {o->d_writer, NCP}, {o->d_staging_rows, T}, {o->d_mixed_locs, T},
       {o->d_token_req, T}, {o->d_topk_offsets, T}, {o->d_segments, 4 * bs},
-      {o->d_prefix_slots, S - NCP}, {o->d_current_slots, NCP}, {o->d_pool_locs, T}};
+      {o->d_prefix_slots, S - NCP}, {o->d_current_slots, NCP}, {o->d_pool_locs, T},
+      {o->d_cur_page_token0, NCP}, {o->d_cur_page_ntok, NCP}};
   for (const Need &e : need) {
     if (e.n > 0 && !e.p) return GPB_EINVAL;
     if (!ok_array(e.p, e.n)) return GPB_EALIGN;
@@ -322,6 +332,7 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
   a.segments = o->d_segments;
   a.prefix_slots = o->d_prefix_slots; a.current_slots = o->d_current_slots;
   a.pool_locs = o->d_pool_locs;
+  a.cur_page_token0 = o->d_cur_page_token0; a.cur_page_ntok = o->d_cur_page_ntok;
   a.status = o->d_status;
 
   hipStream_t st = as_stream(stream);

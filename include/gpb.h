@@ -150,7 +150,9 @@ typedef struct gpb_batch {
  *   current_slots[i]      dense slot of current page i            [NCP]
  *   pool_locs[t]          pool row (KV-cache location) of current token t:
  *                         slot_pages[its slot] * page_size + j mod page_size
- *                                                                       [T] */
+ *                                                                       [T]
+ *   cur_page_token0[i]    first current token held by current page i   [NCP]
+ *   cur_page_ntok[i]      current tokens it holds (1..page_size)       [NCP] */
 typedef struct gpb_plan {
   int32_t *d_slot_base, *d_prefix_span, *d_current_span;
   int32_t *d_q_lens, *d_kv_lens, *d_q_starts;
@@ -161,6 +163,7 @@ typedef struct gpb_plan {
   int32_t *d_staging_rows, *d_mixed_locs;
   int32_t *d_token_req, *d_topk_offsets, *d_segments;
   int32_t *d_prefix_slots, *d_current_slots, *d_pool_locs;
+  int32_t *d_cur_page_token0, *d_cur_page_ntok;
   int32_t *d_status;  /* optional (NULL): GPB_STATUS_* bits the kernels OR in */
 } gpb_plan;
 

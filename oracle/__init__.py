@@ -30,8 +30,9 @@ Parity status per function (pins in tests/test_oracle_pins.py):
   compose_layer, closed_form.dense -- pinned (brute force on tagged rows,
   closed form, library special cases, hand-derived worked example);
   token_req -- pinned to numpy repeat (the repeat_interleave the pages used);
-  prefix_slots, current_slots, pool_locs, gather_slots, fill -- pinned by
-  brute force on tagged rows and against the full gather;
+  prefix_slots, current_slots, pool_locs, cur_page_token0, cur_page_ntok,
+  gather_slots, fill -- pinned by brute force on tagged rows and against the
+  full gather;
   q_lens, kv_lens, q_starts, k_bases, current_bases, q_bases, topk_offsets,
   segments -- the pages give only their names; pinned to the stated
   definitions through the dense and staging geometry they must agree with;
@@ -53,10 +54,11 @@ PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
                "q_starts", "k_bases", "q_bases", "current_bases", "slot_pages",
                "owner", "src", "page_inverse", "staging_page_inverse", "writer",
                "staging_rows", "mixed_locs", "token_req", "topk_offsets", "segments",
-               "prefix_slots", "current_slots", "pool_locs")
+               "prefix_slots", "current_slots", "pool_locs", "cur_page_token0",
+               "cur_page_ntok")
 # the arrays gpbo_plan writes; the next three come from gpbo_token_expansions,
-# the last three from gpbo_prefetch_lists
-_PLAN_CORE = PLAN_FIELDS[:-6]
+# the last five from gpbo_prefetch_lists
+_PLAN_CORE = PLAN_FIELDS[:-8]
 
 
 def _i32(a):
@@ -131,7 +133,8 @@ class Oracle:
                  "staging_page_inverse": n_pool_pages, "writer": NCP,
                  "staging_rows": T, "mixed_locs": T, "token_req": T,
                  "topk_offsets": T, "segments": 4 * bs, "prefix_slots": S - NCP,
-                 "current_slots": NCP, "pool_locs": T}
+                 "current_slots": NCP, "pool_locs": T, "cur_page_token0": NCP,
+                 "cur_page_ntok": NCP}
         # -7 marks entries the oracle never wrote; each array carries a guard
         # tail as long as itself that must stay untouched
         out = {k: np.full(2 * sizes[k] + 64, -7, dtype=np.int32) for k in PLAN_FIELDS}
@@ -151,7 +154,9 @@ class Oracle:
         self.lib.gpbo_prefetch_lists(bs, page_size, pP, pc, pg,
                                      out["prefix_slots"].ctypes.data_as(_I32P),
                                      out["current_slots"].ctypes.data_as(_I32P),
-                                     out["pool_locs"].ctypes.data_as(_I32P))
+                                     out["pool_locs"].ctypes.data_as(_I32P),
+                                     out["cur_page_token0"].ctypes.data_as(_I32P),
+                                     out["cur_page_ntok"].ctypes.data_as(_I32P))
         for k in PLAN_FIELDS:
             assert np.all(out[k][sizes[k]:] == -7), "oracle wrote past " + k
         return {k: out[k][:sizes[k]].copy() for k in PLAN_FIELDS}

@@ -290,17 +290,26 @@ void gpbo_token_expansions(int32_t bs, int32_t page_size,
  *   current_slots[i]  dense slot of current page i           [NCP]
  *   pool_locs[t]      pool row of current token t: its page is the request's
  *                     listed current page j / PS, row j mod PS   [T]
+ *   cur_page_token0[i], cur_page_ntok[i]  the current tokens page i holds:
+ *                     first token index and count (1..PS)       [NCP]
  */
 void gpbo_prefetch_lists(int32_t bs, int32_t page_size,
                          const int32_t *prefix_pages, const int32_t *cur_tokens,
                          const int32_t *req_pages, int32_t *prefix_slots,
-                         int32_t *current_slots, int32_t *pool_locs) {
+                         int32_t *current_slots, int32_t *pool_locs,
+                         int32_t *cur_page_token0, int32_t *cur_page_ntok) {
   int32_t slot = 0, u = 0, i = 0, token = 0;
   for (int32_t r = 0; r < bs; r++) {
     for (int32_t k = 0; k < prefix_pages[r]; k++) prefix_slots[u++] = slot++;
     int32_t first_cur = slot;
     int32_t pages = (int32_t)ceil_div(cur_tokens[r], page_size);
-    for (int32_t k = 0; k < pages; k++) current_slots[i++] = slot++;
+    for (int32_t k = 0; k < pages; k++) {
+      /* current page i holds tokens [token + k*PS, token + min(c, (k+1)*PS)) */
+      cur_page_token0[i] = token + k * page_size;
+      cur_page_ntok[i] = cur_tokens[r] - k * page_size < page_size
+                             ? cur_tokens[r] - k * page_size : page_size;
+      current_slots[i++] = slot++;
+    }
     for (int32_t j = 0; j < cur_tokens[r]; j++)
       pool_locs[token++] = req_pages[first_cur + j / page_size] * page_size + j % page_size;
   }

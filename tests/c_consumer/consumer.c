@@ -126,7 +126,7 @@ static int run(const char *in, const char *out) {
   /* plan outputs in the header's order, with their sizes */
   const int64_t bs = b.bs, npp = b.n_pool_pages;
   const int64_t sizes[] = {bs, 2 * bs, 2 * bs, bs, bs, bs, bs, bs, bs, S, S, S, npp, npp,
-                           NCP, T, T, T, T, 4 * bs, S - NCP, NCP, T};
+                           NCP, T, T, T, T, 4 * bs, S - NCP, NCP, T, NCP, NCP};
   enum { NF = sizeof sizes / sizeof sizes[0] };
   int32_t *outs[NF];
   for (int k = 0; k < NF; k++) HCHECK(hipMalloc((void **)&outs[k], 4 * (size_t)sizes[k] + 4));
@@ -137,7 +137,8 @@ static int run(const char *in, const char *out) {
                           &p.d_page_inverse, &p.d_staging_page_inverse, &p.d_writer,
                           &p.d_staging_rows, &p.d_mixed_locs, &p.d_token_req,
                           &p.d_topk_offsets, &p.d_segments, &p.d_prefix_slots,
-                          &p.d_current_slots, &p.d_pool_locs};
+                          &p.d_current_slots, &p.d_pool_locs, &p.d_cur_page_token0,
+                          &p.d_cur_page_ntok};
   for (int k = 0; k < NF; k++) *fields[k] = outs[k];
   p.d_status = d_status;
 

@@ -299,6 +299,11 @@ def pin_prefetch_split(orc, batch, pl, pool, cur, dense, staging):
         assert np.all(kind[s * PS:(s + 1) * PS] != KIND_POOL)
         assert pl["owner"][s] >= NP and pl["src"][s] == i + 1
     ml = pl["mixed_locs"].astype(np.int64)
+    # the tokens a current page holds: exactly those whose dense row is in it
+    for i, s in enumerate(cur_s):
+        toks = np.nonzero(ml // PS == s)[0]
+        assert pl["cur_page_ntok"][i] == len(toks) and 1 <= len(toks) <= PS
+        assert pl["cur_page_token0"][i] == toks[0] and np.all(np.diff(toks) == 1)
     locs = pl["pool_locs"].astype(np.int64)
     assert np.array_equal(locs // PS, pl["slot_pages"][ml // PS])
     assert np.array_equal(locs % PS, ml % PS)

@@ -56,7 +56,7 @@ def _read_result(path, b):
     S, T, NCP = np.frombuffer(raw[:12], "<i4")
     bs, npp = b.bs, b.n_pool_pages
     sizes = [bs, 2 * bs, 2 * bs, bs, bs, bs, bs, bs, bs, S, S, S, npp, npp, NCP, T, T, T,
-             T, 4 * bs, S - NCP, NCP, T]
+             T, 4 * bs, S - NCP, NCP, T, NCP, NCP]
     at = 12
     plan = {}
     for name, n in zip(oracle.PLAN_FIELDS, sizes):

@@ -136,7 +136,8 @@ def test_single_layer_workloads(orc, name):
     r.run(b.n_layers)
     torch.cuda.synchronize()
     want = _check_plan(b, r, orc)
-    _check_layer(b, r, 0, want, [_host(p) for p in pools], [_host(c) for c in curs], orc)
+    pools_np, curs_np = [_host(p) for p in pools], [_host(c) for c in curs]
+    _check_layer(b, r, 0, want, pools_np, curs_np, orc)
     assert _status(r) == 0
 
 

@@ -54,12 +54,16 @@ MUTANTS = {
                                  "    dense_row += page_size * (pages - prefix_pages[r]);"),
     "segment_kv_len_padded": ("    segments[4 * r + 3] = page_size * prefix_pages[r] + cur_tokens[r];",
                               "    segments[4 * r + 3] = page_size * pages;"),
-    "prefetch_list_skips_empty": ("    for (int32_t k = 0; k < pages; k++) current_slots[i++] = slot++;",
-                                  "    for (int32_t k = 0; k < pages; k++) current_slots[i++] = slot; slot += pages;"),
+    "current_slot_not_advanced": ("      current_slots[i++] = slot++;",
+                                  "      current_slots[i++] = slot;"),
     "pool_loc_wrong_page": ("      pool_locs[token++] = req_pages[first_cur + j / page_size] * page_size + j % page_size;",
                             "      pool_locs[token++] = req_pages[first_cur] * page_size + j % page_size;"),
     "gather_slots_uses_k": ("    int32_t s = slots[k];", "    int32_t s = k;"),
     "fill_skips_pool": ("    else memcpy(pool + q * RB, row, (size_t)RB);", "    else (void)q;"),
+    "page_ntok_full_pages": ("                             ? cur_tokens[r] - k * page_size : page_size;",
+                             "                             ? page_size : page_size;"),
+    "page_token0_unpaged": ("      cur_page_token0[i] = token + k * page_size;",
+                            "      cur_page_token0[i] = token + k;"),
     "stray_row_not_flagged": ("if (row < 0 || row >= n_staging_rows) { bad = 1; continue; }",
                               "if (row < 0 || row >= n_staging_rows) { continue; }"),
 }
