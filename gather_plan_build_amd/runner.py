@@ -58,8 +58,10 @@ class ComposeRunner:
         self.staging_rows_total = self.w * self.cap * self.ps
         slab = self.cap * self.ps * self.rb
         dev = torch.device(device)
-        self.staging = [torch.empty(self.staging_rows_total * self.rb, dtype=torch.uint8,
-                                    device=dev) for _ in range(PARITY)]
+        # both parity halves in one allocation, so one launch clears them
+        half = self.staging_rows_total * self.rb
+        self.staging_all = torch.empty(PARITY * half, dtype=torch.uint8, device=dev)
+        self.staging = [self.staging_all[h * half:(h + 1) * half] for h in range(PARITY)]
         self.dense = [torch.empty(max(self.S * self.ps * self.rb, 16), dtype=torch.uint8,
                                   device=dev) for _ in range(PARITY)]
         # buffers passed to the kernels must hold what the kernels address
@@ -79,8 +81,7 @@ class ComposeRunner:
         staging halves (once per batch)."""
         if self.owns_plan:
             self.plan.build(stream)
-        for h in range(PARITY):
-            B.staging_clear(self.staging[h], stream=stream)
+        B.staging_clear(self.staging_all, stream=stream)
 
     def scatter(self, layer, stream=None):
         h, k = layer % PARITY, layer % len(self.curs)
