@@ -38,7 +38,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="traced",
                     choices=["traced", "opaque", "medium", "multi_source", "tiny"])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU oracle sample (0 disables it)")
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE", "FETCH", "WRITE"),
                     help="write profiles/ summaries from three rocprofv3 csv output "
@@ -98,8 +98,11 @@ def cpu_baseline(batch, pools, curs, budget_s):
     host_pools, host_curs = {}, {}
     per_layer = []
     spent = 0.0
-    layer = 0
-    while layer < batch.n_layers and (spent < budget_s or layer == 0):
+    runs = 0
+    # cycle through the batch's layers until the budget is spent (at least
+    # one pass over every layer)
+    while spent < budget_s or runs < batch.n_layers:
+        layer = runs % batch.n_layers
         k = layer % len(pools)
         if k not in host_pools:
             host_pools[k] = pools[k].cpu().numpy().reshape(-1)
@@ -109,7 +112,7 @@ def cpu_baseline(batch, pools, curs, budget_s):
         dt = time.perf_counter() - t0
         per_layer.append(dt)
         spent += dt
-        layer += 1
+        runs += 1
     S, T = batch.n_req_pages, batch.n_cur_tokens
     PS, RB = batch.page_size, batch.row_bytes
     layer_bytes = (2 * S * PS * RB + 2 * T * RB + 8 * S + 4 * T
@@ -119,10 +122,10 @@ def cpu_baseline(batch, pools, curs, budget_s):
             "kind": "oracle",
             "us_per_layer": round(med * 1e6, 1),
             "plan_us": round(plan_s * 1e6, 1),
-            "sample": "%d of %d layers of the %s workload (median per layer; plan "
-                      "once), single-threaded C oracle: zero staging, scatter "
-                      "current rows, gather every page" % (len(per_layer),
-                                                           batch.n_layers, batch.name),
+            "sample": "%d layer runs (the %s workload's %d layers, cycled; %.1f s of "
+                      "CPU work; median per layer; plan once), single-threaded C "
+                      "oracle: zero staging, scatter current rows, gather every page"
+                      % (runs, batch.name, batch.n_layers, spent),
             "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
 
 
