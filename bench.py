@@ -85,30 +85,48 @@ def _traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(batch, pools, curs, budget_s):
-    """The CPU oracle (plain C loops, one thread) on the same batch: the plan
-    once, then layers until the budget is spent.  Returns the JSON object."""
+def _host_threads():
+    """Worker threads for the parallel oracle leg: the cores this process may
+    run on, at most 16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(batch, pools, curs, budget_s, threads=None):
+    """The CPU oracle (plain C loops) on the same batch: the plan once, then
+    layers until the budget is spent, first on one thread, then as
+    ``threads`` concurrent copies of the same single-threaded oracle (each
+    with its own staging and dense buffers, layers dealt round-robin) for
+    half the budget.  Returns the JSON object; its headline is the
+    single-threaded figure, the concurrent one sits under "threaded"."""
+    import threading
     import numpy as np
     import oracle
     orc = oracle.default()
     t0 = time.perf_counter()
     want = oracle.plan_for(batch, orc)
     plan_s = time.perf_counter() - t0
-    staging = np.empty(batch.staging_rows_total * batch.row_bytes, np.uint8)
     host_pools, host_curs = {}, {}
+    for k in range(min(len(pools), batch.n_layers)):
+        host_pools[k] = pools[k].cpu().numpy().reshape(-1)
+        host_curs[k] = curs[k].cpu().numpy()
+
+    def run_layer(layer, staging):
+        k = layer % len(pools)
+        oracle.layer_for(batch, want, host_pools[k], host_curs[k], staging, orc)
+
+    staging = np.empty(batch.staging_rows_total * batch.row_bytes, np.uint8)
     per_layer = []
     spent = 0.0
     runs = 0
     # cycle through the batch's layers until the budget is spent (at least
     # one pass over every layer)
     while spent < budget_s or runs < batch.n_layers:
-        layer = runs % batch.n_layers
-        k = layer % len(pools)
-        if k not in host_pools:
-            host_pools[k] = pools[k].cpu().numpy().reshape(-1)
-            host_curs[k] = curs[k].cpu().numpy()
         t0 = time.perf_counter()
-        oracle.layer_for(batch, want, host_pools[k], host_curs[k], staging, orc)
+        run_layer(runs % batch.n_layers, staging)
         dt = time.perf_counter() - t0
         per_layer.append(dt)
         spent += dt
@@ -118,15 +136,51 @@ def cpu_baseline(batch, pools, curs, budget_s):
     layer_bytes = (2 * S * PS * RB + 2 * T * RB + 8 * S + 4 * T
                    + 8 * (batch.n_pool_entries + batch.n_writers))
     med = sorted(per_layer)[len(per_layer) // 2]
-    return {"value": round(layer_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "us_per_layer": round(med * 1e6, 1),
-            "plan_us": round(plan_s * 1e6, 1),
-            "sample": "%d layer runs (the %s workload's %d layers, cycled; %.1f s of "
-                      "CPU work; median per layer; plan once), single-threaded C "
-                      "oracle: zero staging, scatter current rows, gather every page"
-                      % (runs, batch.name, batch.n_layers, spent),
-            "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
+    out = {"value": round(layer_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "us_per_layer": round(med * 1e6, 1),
+           "plan_us": round(plan_s * 1e6, 1),
+           "sample": "%d layer runs (the %s workload's %d layers, cycled; %.1f s of "
+                     "CPU work; median per layer; plan once), single-threaded C "
+                     "oracle: zero staging, scatter current rows, gather every page"
+                     % (runs, batch.name, batch.n_layers, spent),
+           "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
+
+    n = threads if threads is not None else _host_threads()
+    if n > 1:
+        # the oracle's C calls release the GIL (ctypes), so the copies run
+        # concurrently; all start together and run for the same wall time
+        done = [0] * n
+        seconds = max(budget_s / 2, 1e-3)
+        barrier = threading.Barrier(n + 1)
+
+        def worker(w):
+            st = np.empty(batch.staging_rows_total * batch.row_bytes, np.uint8)
+            run_layer(w % batch.n_layers, st)  # untimed: first touch of its buffers
+            barrier.wait()
+            deadline = time.perf_counter() + seconds
+            layer = w
+            while time.perf_counter() < deadline:
+                run_layer(layer % batch.n_layers, st)
+                done[w] += 1
+                layer += n
+
+        pool = [threading.Thread(target=worker, args=(w,)) for w in range(n)]
+        for t in pool:
+            t.start()
+        barrier.wait()
+        t0 = time.perf_counter()
+        for t in pool:
+            t.join()
+        wall = time.perf_counter() - t0
+        total = sum(done)
+        out["threaded"] = {
+            "value": round(layer_bytes * total / wall / 1e9, 3), "unit": "GB/s",
+            "cores": n, "kind": "oracle",
+            "sample": "%d layer runs over %.1f s wall on %d threads, each a copy of "
+                      "the single-threaded oracle with its own staging and dense "
+                      "buffers" % (total, wall, n)}
+    return out
 
 
 def _cpu_model():
@@ -164,19 +218,27 @@ def _short(name):
     return name[:60]
 
 
+# $REPO is the repository root, $OUT the directory the three runs write to
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py "
+             "-d $OUT/prof_trace -o trace -- python3 $REPO/bench.py "
              "--steps 3 --warmup 1 --cpu-seconds 0 --no-extras",
     "fetch": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv "
-             "-d $REPO/gpurun_out/prof_fetch -o fetch -- python3 $REPO/bench.py "
+             "-d $OUT/prof_fetch -o fetch -- python3 $REPO/bench.py "
              "--steps 1 --warmup 0 --cpu-seconds 0 --no-extras --calibration-copy-mib 1024",
     "write": "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv "
-             "-d $REPO/gpurun_out/prof_write -o write -- python3 $REPO/bench.py "
+             "-d $OUT/prof_write -o write -- python3 $REPO/bench.py "
              "--steps 1 --warmup 0 --cpu-seconds 0 --no-extras --calibration-copy-mib 1024",
-    "summary": "python3 bench.py --summarize-profiles gpurun_out/prof_trace "
-               "gpurun_out/prof_fetch gpurun_out/prof_write",
+    "summary": "python3 bench.py --summarize-profiles $OUT/prof_trace "
+               "$OUT/prof_fetch $OUT/prof_write",
 }
+
+
+def _profile_commands(trace_dir):
+    """PROFILE_COMMANDS with $OUT set to the directory the runs wrote to."""
+    out = os.path.relpath(os.path.dirname(os.path.abspath(trace_dir)), ROOT)
+    return {k: v.replace("$OUT", "$REPO/" + out if k != "summary" else out)
+            for k, v in PROFILE_COMMANDS.items()}
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
@@ -188,7 +250,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     lines = ["# rocprofv3 kernel statistics, %s workload (bench.py)" % workload,
-             "# command: " + PROFILE_COMMANDS["trace"],
+             "# command: " + _profile_commands(trace_dir)["trace"],
              "# source digest of %s: %s" % (", ".join(DIGEST_FILES), _source_digest()),
              "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
@@ -215,7 +277,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     f_copy, w_copy = max(fetch["copyBuffer"]), max(write["copyBuffer"])
     f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
     rec = {"workload": workload, "source_digest": _source_digest(),
-           "commands": PROFILE_COMMANDS,
+           "commands": _profile_commands(trace_dir),
            "calibration": {"copy_bytes": int(copy_kib * 1024), "fetch_kib": f_copy,
                            "write_kib": w_copy, "fetch_scale": f_scale,
                            "write_scale": w_scale},
