@@ -1,5 +1,5 @@
-// compose.hip -- per-layer current-row scatter and slot-dense page gather,
-// plus the per-batch staging clear (gfx950).
+// compose.hip -- per-layer current-row scatter and slot-dense page gather
+// (gfx950).
 //
 // Page d63fbd4, commit "current rows written straight into staging": per
 // layer, one index_copy_ of the current token rows into the zeroed staging
@@ -145,37 +145,6 @@ __global__ __launch_bounds__(B) void k_row_scatter(
   }
   if (bad && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
 }
-
-// Flat: lane g of the grid zeroes chunks g, g + 256, g + 512, g + 768 of its
-// workgroup's 1024-chunk range.
-__global__ __launch_bounds__(kBlock) void k_fill_zero(u32x4 *__restrict__ p,
-                                                      int64_t n_chunks) {
-  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * 4) + threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t i = first + k * kBlock;
-    if (i < n_chunks) __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, p + i);
-  }
-}
-
-}  // namespace
-}  // namespace gpb
-
-extern "C" int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream) {
-  using namespace gpb;
-  if (n_bytes < 0) return GPB_EINVAL;
-  if (n_bytes == 0) return GPB_OK;
-  if (!d_ptr) return GPB_EINVAL;
-  if (n_bytes % 16 != 0 || !aligned(d_ptr, 16)) return GPB_EALIGN;
-  const int64_t chunks = n_bytes / 16;
-  const int64_t grid = ceil_div64(chunks, kBlock * 4);
-  if (grid > INT32_MAX) return GPB_ERANGE;
-  return launch(k_fill_zero, dim3(static_cast<uint32_t>(grid)), dim3(kBlock),
-                as_stream(stream), static_cast<u32x4 *>(d_ptr), chunks);
-}
-
-namespace gpb {
-namespace {
 
 int launch_rows(void *d_staging, int64_t n_staging_rows, const int32_t *d_staging_rows,
                 void *d_pool, int64_t n_pool_rows, const int32_t *d_pool_locs,

@@ -364,14 +364,18 @@ def test_out_of_range_staging_rows_are_skipped(orc):
     assert int(status.item()) == gpb.STATUS_BAD_STAGING_ROW
 
 
-def test_staging_clear_zeroes_exactly(orc):
+@pytest.mark.parametrize("start,n", [(16, 4096 * 37), (16, 16), (48, 4096 * 37 + 16 * 5),
+                                     (0, 4080), (4096, 4112), (32, 3 * 4096 - 16)])
+def test_staging_clear_zeroes_exactly(orc, start, n):
+    """Exactly [start, start + n) becomes zero, including a last workgroup
+    that covers less than its 4 KiB."""
     gpb = _gpb()
     buf = torch.full((1 << 20,), 0xEE, dtype=torch.uint8, device="cuda")
-    gpb.staging_clear(buf[16:16 + 4096 * 37], 4096 * 37)
+    gpb.staging_clear(buf[start:start + n], n)
     torch.cuda.synchronize()
     h = _host(buf)
-    assert not h[16:16 + 4096 * 37].any()
-    assert (h[:16] == 0xEE).all() and (h[16 + 4096 * 37:] == 0xEE).all()
+    assert not h[start:start + n].any()
+    assert (h[:start] == 0xEE).all() and (h[start + n:] == 0xEE).all()
 
 
 def test_index_key_twin_shares_the_plan(orc):
