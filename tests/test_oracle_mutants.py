@@ -66,6 +66,31 @@ MUTANTS = {
                             "      cur_page_token0[i] = token + k;"),
     "stray_row_not_flagged": ("if (row < 0 || row >= n_staging_rows) { bad = 1; continue; }",
                               "if (row < 0 || row >= n_staging_rows) { continue; }"),
+    "staging_rows_via_page_inverse": (
+        "staging_rows[t] = staging_page_inverse[loc / PS] * PS + loc % PS;",
+        "staging_rows[t] = page_inverse[loc / PS] * PS + loc % PS;"),
+    "staging_row_drops_offset": (
+        "staging_rows[t] = staging_page_inverse[loc / PS] * PS + loc % PS;",
+        "staging_rows[t] = staging_page_inverse[loc / PS] * PS;"),
+    "slab_stride_short": ("= w * CAP + i + 1;", "= w * (CAP - 1) + i + 1;"),
+    "current_span_starts_at_base": (
+        "current_span[2 * r + 0] = running_slots + prefix_pages[r];",
+        "current_span[2 * r + 0] = running_slots;"),
+    "q_lens_in_pages": ("q_lens[r] = cur_tokens[r];", "q_lens[r] = C;"),
+    "page_inverse_off_by_one": ("page_inverse[slot_pages[s]] = s;",
+                                "page_inverse[slot_pages[s]] = s + 1;"),
+    "counts_drop_prefix": ("S += prefix_pages[r] + C;", "S += C;"),
+    "segment_first_row_is_token": ("segments[4 * r + 2] = dense_row;",
+                                   "segments[4 * r + 2] = token;"),
+    "prefix_slot_not_advanced": ("prefix_slots[u++] = slot++;", "prefix_slots[u++] = slot;"),
+    "fill_skips_staging": ("else memcpy(staging + d * RB, row, (size_t)RB);",
+                           "else (void)d;"),
+    # the variant reads seen[n_pool_pages], one byte past a heap block: it lands
+    # in malloc's rounding or the next block's header, never outside the heap
+    "last_page_accepted": ("if (p < 1 || p >= n_pool_pages || seen[p])",
+                           "if (p < 1 || p > n_pool_pages || seen[p])"),
+    "slot_pages_reversed": ("slot_pages[s] = req_pages[s];",
+                            "slot_pages[s] = req_pages[S - 1 - s];"),
 }
 
 CHILD = r"""
