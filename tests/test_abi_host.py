@@ -228,3 +228,41 @@ def test_validation_agrees_with_oracle_on_random_batches(orc):
 
 def pins_random(rng, n):
     return [workloads.random_batch(rng) for _ in range(n)]
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    """With libgpb.so absent the package raises at import: there is no CPU
+    path to fall back on."""
+    import subprocess
+    import sys
+    code = ("import os, sys; sys.path.insert(0, %r)\n"
+            "try:\n"
+            "    import gather_plan_build_amd\n"
+            "except ImportError as e:\n"
+            "    print('RAISED', e); sys.exit(0)\n"
+            "sys.exit(5)\n" % ROOT)
+    env = dict(os.environ, GPB_LIB=str(tmp_path / "missing" / "libgpb.so"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "RAISED" in r.stdout and "no fallback" in r.stdout
+
+
+def test_product_sources_never_reach_the_oracle():
+    """The package, its HIP sources and the header name no oracle module,
+    file or symbol."""
+    import re
+    pat = re.compile(r"\boracle\b|gpbo_|liboracle|gpb_oracle")
+    roots = [os.path.join(ROOT, "gather_plan_build_amd"), os.path.join(ROOT, "include")]
+    hits = []
+    for top in roots:
+        for dirpath, _, files in os.walk(top):
+            for name in files:
+                if not name.endswith((".py", ".hip", ".h", ".c", ".cpp")):
+                    continue
+                path = os.path.join(dirpath, name)
+                with open(path, encoding="utf-8") as f:
+                    for n, line in enumerate(f, 1):
+                        if pat.search(line):
+                            hits.append("%s:%d: %s" % (path, n, line.strip()))
+    assert not hits, "\n".join(hits)
