@@ -128,6 +128,14 @@ def test_gather_argument_checks():
     empty = B.gpb_sources()
     assert f(a, ctypes.byref(empty), a, a, 4, 64, 1152, None, None) == B.EINVAL
     assert f(a, ctypes.byref(good.c), a, a, 4, 1 << 20, 4096, None, None) == B.ERANGE
+    # the table holds at most GPB_MAX_SOURCES entries
+    full = B.Sources([(a, 10)] * B.MAX_SOURCES)
+    assert f(a, ctypes.byref(full.c), a, a, 0, 64, 1152, None, None) == B.OK
+    over = B.gpb_sources()
+    over.n = B.MAX_SOURCES + 1
+    assert f(a, ctypes.byref(over), a, a, 4, 64, 1152, None, None) == B.EINVAL
+    with pytest.raises(B.GpbError):
+        B.Sources([(a, 10)] * (B.MAX_SOURCES + 1))
 
 
 def test_slot_gather_and_fill_argument_checks():

@@ -254,6 +254,29 @@ def test_row_and_page_geometry(orc, ps, rb):
         _random_case(orc, b)
 
 
+def _full_table_batch():
+    """The largest pointer table the ABI takes: 32 pool entries and 32 staging
+    slabs (64 entries), with 51 current pages dealt round robin over the 32
+    writers, 4-token pages and 48-byte rows."""
+    rng = np.random.default_rng(64)
+    P = np.array([3, 0, 2, 5, 1, 0, 4, 2], np.int32)
+    c = np.array([37, 20, 0, 9, 64, 3, 17, 41], np.int32)
+    PS, RB, NP, W = 4, 48, 32, 32
+    need = int(P.sum() + ((c + PS - 1) // PS).sum())
+    n_pool = need + 40
+    pages = rng.choice(np.arange(1, n_pool), size=need, replace=False).astype(np.int32)
+    cap = workloads.staging_cap_for(int(c.sum()), len(P), PS)
+    return workloads.Batch("full_table", len(P), PS, RB, n_pool, NP, W, cap, P, c, pages)
+
+
+def test_full_pointer_table(orc):
+    b = _full_table_batch()
+    assert b.n_pool_entries + b.n_writers == 64
+    assert int(((b.cur_tokens + b.page_size - 1) // b.page_size).sum()) > b.n_writers
+    _say("full table: 64 entries, slots", b.n_req_pages, "tokens", b.n_cur_tokens)
+    _random_case(orc, b)
+
+
 def test_empty_and_degenerate_batches(orc):
     cases = [([], []), ([0, 0], [0, 0]), ([3, 2], [0, 0]), ([0, 0], [5, 64]),
              ([1], [65])]

@@ -27,7 +27,7 @@ def test_random_batches(orc, seed):
         pins.check_batch(orc, b)
 
 
-@pytest.mark.parametrize("W,NP", [(2, 1), (3, 2), (8, 8)])
+@pytest.mark.parametrize("W,NP", [(2, 1), (3, 2), (8, 8), (32, 32)])
 def test_multi_writer_batches(orc, W, NP):
     for b in pins.random_batches(25, seed=100 + W, n_writers=W, n_pool_entries=NP):
         pins.check_batch(orc, b)
