@@ -7,12 +7,22 @@
 #define GPB_LOAD_POLICY 2      // cache-policy bits of the buffer loads (nt)
 #endif
 #ifndef GPB_STORE_POLICY
-// cache-policy bits of the buffer stores: sc1.  Measured on the traced
-// workload (interleaved runs, 30 steps each): sc1 on every per-layer store
-// 93.7 us per layer, nt 94.5 us, sc1 on the scatter alone 94.8 us (the scatter
-// itself is 5% faster with sc1, but mixed policies cost more between the two
-// kernels than that saves).
+// cache-policy bits of the row stores (scatter, fused fill, staging clear):
+// sc1.  Measured on the traced workload (interleaved runs, 30 steps each): the
+// scatter takes 16.0 us with sc1 and 16.8-17.1 us with nt or nt|sc1.
 #define GPB_STORE_POLICY 16
+#endif
+#ifndef GPB_DENSE_STORE_POLICY
+// cache-policy bits of the gather's dense-page stores: nt|sc1.  Interleaved
+// A/B on MI355X, 3 runs of 30 steps per variant, scatter stores sc1 in all:
+//   dense stores   traced us/layer   opaque us/layer
+//   sc1            93.45             169.1
+//   nt             94.78             165.3
+//   nt|sc1         93.02-93.23       163.5-163.6
+//   nt|sc0|sc1     93.24             163.4
+//   sc0|sc1        93.82             169.4
+//   nt|sc0         94.88             165.1
+#define GPB_DENSE_STORE_POLICY 18
 #endif
 
 namespace gpb {
@@ -33,6 +43,9 @@ __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void st16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, GPB_STORE_POLICY);
+}
+__device__ __forceinline__ void st16_dense(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, GPB_DENSE_STORE_POLICY);
 }
 
 }  // namespace gpb

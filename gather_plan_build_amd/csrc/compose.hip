@@ -18,8 +18,9 @@
 //     default), walked in address order: on MI355X this measured faster than
 //     fewer, larger units (more chunks in flight per lane, 256-lane
 //     workgroups), than part-major orders and than XCD-blocked orders;
-//   - loads are non-temporal (each byte is read once per layer); stores carry
-//     the sc1 policy bit, measured faster than non-temporal stores here;
+//   - loads are non-temporal (each byte is read once per layer); the dense
+//     stores carry nt|sc1 and the staging stores sc1, each measured fastest
+//     for its kernel here;
 //   - raw buffer resources bound every access, so ragged tails, -1 sentinels
 //     and bad rows cost no branches.
 // The unit shape and cache-policy bits can be overridden at build time
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(B) void k_compose_gather(
 #pragma unroll
   for (int k = 0; k < CPT; ++k) v[k] = ld16(rs, first + k * (B * 16));
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) st16(v[k], rd, first + k * (B * 16));
+  for (int k = 0; k < CPT; ++k) st16_dense(v[k], rd, first + k * (B * 16));
   if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
     atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
 }

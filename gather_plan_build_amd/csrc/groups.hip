@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kUnitLanes) void k_gather_groups(
   const __amdgpu_buffer_rsrc_t rd =
       rsrc(gr.dense + static_cast<int64_t>(slot) * gr.page_bytes, gr.page_bytes);
   const uint32_t off = (static_cast<uint32_t>(part) * kUnitLanes + threadIdx.x) * 16u;
-  st16(ld16(rs, off), rd, off);
+  st16_dense(ld16(rs, off), rd, off);
   if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
     atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
 }
