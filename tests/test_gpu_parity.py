@@ -246,7 +246,10 @@ def test_many_requests_past_the_lds_stage(orc):
     _random_case(orc, b)
 
 
-@pytest.mark.parametrize("ps,rb", [(1, 16), (2, 4096 + 16), (64, 656), (64, 1152), (3, 48)])
+# 336-byte rows (21 chunks) are the smallest whose scatter workgroups fetch
+# their staging rows as scalars; 320-byte rows (20 chunks) take the per-lane path
+@pytest.mark.parametrize("ps,rb", [(1, 16), (2, 4096 + 16), (64, 656), (64, 1152), (3, 48),
+                                   (5, 336), (5, 320)])
 def test_row_and_page_geometry(orc, ps, rb):
     rng = np.random.default_rng(ps * 7 + rb)
     for b in [workloads.random_batch(rng, page_size=ps, row_bytes=rb, max_pool=40)
