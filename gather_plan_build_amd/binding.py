@@ -144,12 +144,25 @@ def _check(rc, what):
 
 
 def _ptr(x):
-    """Device address of a torch tensor, or an int address, or None."""
+    """Device address of a GPU torch tensor, or an int address (taken as a
+    device address), or None.  A tensor in host memory is refused: its address
+    would reach a kernel."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError("a %s tensor in host memory was passed where device memory "
+                         "is required" % (tuple(x.shape),))
     return x.data_ptr()
+
+
+def _gpu_device(device):
+    import torch
+    dev = torch.device(device)
+    if dev.type != "cuda":
+        raise ValueError("the compose runs on the GPU: device %s is not a GPU device" % dev)
+    return dev
 
 
 def _stream(stream):
@@ -162,7 +175,12 @@ def _stream(stream):
 
 
 def _host_i32(a):
-    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
+    """Contiguous int32 copy of host metadata; values outside int32 raise
+    instead of wrapping."""
+    v = np.asarray(a, dtype=np.int64).reshape(-1)
+    if v.size and (v.min() < np.iinfo(np.int32).min or v.max() > np.iinfo(np.int32).max):
+        raise ValueError("batch metadata value outside int32")
+    return np.ascontiguousarray(v.astype(np.int32))
 
 
 class BatchMeta:
@@ -208,7 +226,7 @@ class Plan:
         self.meta = meta
         self.S, self.T, self.NCP = plan_sizes(meta)
         b = meta.c
-        dev = torch.device(device)
+        dev = _gpu_device(device)
         self.d_prefix = torch.from_numpy(meta.h_prefix).to(dev)
         self.d_cur = torch.from_numpy(meta.h_cur).to(dev)
         self.d_req = torch.from_numpy(meta.h_req).to(dev)

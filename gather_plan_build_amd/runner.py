@@ -12,11 +12,24 @@ On one GPU every pool entry of the table is the layer's own pool arena and
 every staging entry is a slab carved from the local staging region; stream
 order replaces the cross-GPU barrier.
 """
+import numpy as np
 import torch
 
 from . import binding as B
 
 PARITY = 2
+
+
+def _check_arena(t, n_bytes, what):
+    """An arena the kernels read whole: contiguous uint8 device memory of
+    exactly n_bytes."""
+    if not t.is_cuda:
+        raise ValueError("%s: the tensor is in host memory, the kernels need device "
+                         "memory" % what)
+    if t.dtype != torch.uint8 or not t.is_contiguous() or t.numel() != n_bytes:
+        raise ValueError("%s: need a contiguous uint8 tensor of %d bytes, got %s %s%s"
+                         % (what, n_bytes, t.dtype, tuple(t.shape),
+                            "" if t.is_contiguous() else " (not contiguous)"))
 
 
 class ComposeRunner:
@@ -38,35 +51,35 @@ class ComposeRunner:
             # batch's plan: no plan array depends on the row size
             B.plan_sizes(meta)
             m = plan.meta.c
-            assert (m.bs, m.page_size, m.n_pool_pages, m.n_pool_entries, m.n_writers,
-                    m.staging_cap_pages) == (b.bs, b.page_size, b.n_pool_pages,
-                                             b.n_pool_entries, b.n_writers,
-                                             b.staging_cap_pages)
-            assert (plan.meta.h_prefix == meta.h_prefix).all()
-            assert (plan.meta.h_cur == meta.h_cur).all()
-            assert (plan.meta.h_req == meta.h_req).all()
+            same = ((m.bs, m.page_size, m.n_pool_pages, m.n_pool_entries, m.n_writers,
+                     m.staging_cap_pages) == (b.bs, b.page_size, b.n_pool_pages,
+                                              b.n_pool_entries, b.n_writers,
+                                              b.staging_cap_pages)
+                    and np.array_equal(plan.meta.h_prefix, meta.h_prefix)
+                    and np.array_equal(plan.meta.h_cur, meta.h_cur)
+                    and np.array_equal(plan.meta.h_req, meta.h_req))
+            if not same:
+                raise ValueError("a shared plan must come from the same batch metadata "
+                                 "(only the row size may differ)")
         self.plan = plan
         self.owns_plan = plan.meta is meta
         self.S, self.T = self.plan.S, self.plan.T
         self.pools, self.curs = list(pools), list(curs)
+        if not self.pools or not self.curs:
+            raise ValueError("at least one pool arena and one current-row arena")
         for p in self.pools:
-            assert p.dtype == torch.uint8 and p.is_contiguous()
-            assert p.numel() == self.n_pool_pages * self.ps * self.rb
+            _check_arena(p, self.n_pool_pages * self.ps * self.rb, "pool arena")
         for c in self.curs:
-            assert c.dtype == torch.uint8 and c.is_contiguous()
-            assert c.numel() == self.T * self.rb
+            _check_arena(c, self.T * self.rb, "current rows")
         self.staging_rows_total = self.w * self.cap * self.ps
         slab = self.cap * self.ps * self.rb
-        dev = torch.device(device)
+        dev = B._gpu_device(device)
         # both parity halves in one allocation, so one launch clears them
         half = self.staging_rows_total * self.rb
         self.staging_all = torch.empty(PARITY * half, dtype=torch.uint8, device=dev)
         self.staging = [self.staging_all[h * half:(h + 1) * half] for h in range(PARITY)]
         self.dense = [torch.empty(max(self.S * self.ps * self.rb, 16), dtype=torch.uint8,
                                   device=dev) for _ in range(PARITY)]
-        # buffers passed to the kernels must hold what the kernels address
-        assert self.staging[0].numel() >= self.staging_rows_total * self.rb
-        assert self.dense[0].numel() >= self.S * self.ps * self.rb
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.tables = {}
         for k, pool in enumerate(self.pools):
@@ -171,8 +184,8 @@ def layer_groups(runners, layer, stream=None):
     its index-key twin): one scatter launch and one gather launch for all of
     them."""
     r0 = runners[0]
-    for r in runners[1:]:
-        assert r.plan is r0.plan
+    if any(r.plan is not r0.plan for r in runners[1:]):
+        raise ValueError("grouped formats must share one plan")
     h = layer % PARITY
     t = r0.plan.t
     B.current_row_scatter_groups(

@@ -274,3 +274,25 @@ def test_product_sources_never_reach_the_oracle():
                         if pat.search(line):
                             hits.append("%s:%d: %s" % (path, n, line.strip()))
     assert not hits, "\n".join(hits)
+
+
+def test_host_memory_never_reaches_a_kernel():
+    """Tensors in host memory and non-GPU devices are refused by the binding
+    before any call into the library."""
+    import torch
+    cpu = torch.zeros(4096, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        gpb.staging_clear(cpu)
+    with pytest.raises(ValueError):
+        B._ptr(cpu)
+    b = workloads.make_batch("tiny")
+    with pytest.raises(ValueError):
+        gpb.Plan(gpb.BatchMeta.of(b), device="cpu")
+    pools, curs = workloads.make_values(b, device="cpu")
+    with pytest.raises(ValueError):
+        gpb.ComposeRunner(gpb.BatchMeta.of(b), pools, curs, device="cpu")
+
+
+def test_metadata_outside_int32_is_refused():
+    with pytest.raises(ValueError):
+        gpb.BatchMeta(1, 64, 1152, 16, 1, 1, 4, [2 ** 32 + 1], [0], [1])
