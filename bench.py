@@ -234,11 +234,16 @@ PROFILE_COMMANDS = {
 }
 
 
-def _profile_commands(trace_dir):
-    """PROFILE_COMMANDS with $OUT set to the directory the runs wrote to."""
+def _profile_commands(trace_dir, workload="traced"):
+    """PROFILE_COMMANDS with $OUT set to the directory the runs wrote to, for
+    the given workload."""
     out = os.path.relpath(os.path.dirname(os.path.abspath(trace_dir)), ROOT)
-    return {k: v.replace("$OUT", "$REPO/" + out if k != "summary" else out)
-            for k, v in PROFILE_COMMANDS.items()}
+    flag = "" if workload == "traced" else " --workload " + workload
+    cmds = {}
+    for k, v in PROFILE_COMMANDS.items():
+        v = v.replace("$OUT", "$REPO/" + out if k != "summary" else out)
+        cmds[k] = (v + flag) if k == "summary" else v.replace("bench.py", "bench.py" + flag, 1)
+    return cmds
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
@@ -250,7 +255,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     lines = ["# rocprofv3 kernel statistics, %s workload (bench.py)" % workload,
-             "# command: " + _profile_commands(trace_dir)["trace"],
+             "# command: " + _profile_commands(trace_dir, workload)["trace"],
              "# source digest of %s: %s" % (", ".join(DIGEST_FILES), _source_digest()),
              "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
@@ -277,7 +282,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     f_copy, w_copy = max(fetch["copyBuffer"]), max(write["copyBuffer"])
     f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
     rec = {"workload": workload, "source_digest": _source_digest(),
-           "commands": _profile_commands(trace_dir),
+           "commands": _profile_commands(trace_dir, workload),
            "calibration": {"copy_bytes": int(copy_kib * 1024), "fetch_kib": f_copy,
                            "write_kib": w_copy, "fetch_scale": f_scale,
                            "write_scale": w_scale},
