@@ -68,6 +68,22 @@ def _status(r):
     return int(r.status.item())
 
 
+POISON = 0xA5
+
+
+def _run_poisoned(r, n_layers):
+    """The batch as bench.py runs it (plan build, staging clear, then scatter
+    and gather per layer), with the dense half of each of the last two layers
+    filled with a sentinel byte just before that layer runs.  A dense byte the
+    gather fails to write then shows as a mismatch instead of passing on the
+    identical bytes an earlier layer left in the same half."""
+    r.begin_batch()
+    for layer in range(n_layers):
+        if layer >= n_layers - 2:
+            r.dense[layer % 2].fill_(POISON)
+        r.layer(layer)
+
+
 def test_ragged_tails_stay_inside_their_ranges(orc):
     """Pages whose chunk count is not a multiple of a workgroup's unit (656-
     and 48-byte rows) and a scatter whose last workgroup runs past the last
@@ -120,7 +136,7 @@ def test_tiny_layer_byte_exact(orc):
     b = workloads.make_batch("tiny")
     pools, curs = workloads.make_values(b, device="cuda")
     r = _runner(b, pools, curs)
-    r.run(1)
+    _run_poisoned(r, 1)
     torch.cuda.synchronize()
     want = _check_plan(b, r, orc)
     _check_layer(b, r, 0, want, [_host(p) for p in pools], [_host(c) for c in curs], orc)
@@ -133,7 +149,7 @@ def test_single_layer_workloads(orc, name):
     _say(name, "slots", b.n_req_pages, "tokens", b.n_cur_tokens)
     pools, curs = workloads.make_values(b, device="cuda")
     r = _runner(b, pools, curs)
-    r.run(b.n_layers)
+    _run_poisoned(r, b.n_layers)
     torch.cuda.synchronize()
     want = _check_plan(b, r, orc)
     pools_np, curs_np = [_host(p) for p in pools], [_host(c) for c in curs]
@@ -156,11 +172,12 @@ def test_multi_layer_workloads(orc, name):
     torch.cuda.synchronize()
     want = _check_plan(b, r, orc)
     for layer in range(4):
+        r.dense[layer % 2].fill_(POISON)
         r.layer(layer)
         torch.cuda.synchronize()
         _check_layer(b, r, layer, want, pools_np, curs_np, orc)
         _say("  layer", layer, "ok")
-    r.run(b.n_layers)
+    _run_poisoned(r, b.n_layers)
     torch.cuda.synchronize()
     for layer in (b.n_layers - 2, b.n_layers - 1):
         _check_layer(b, r, layer, want, pools_np, curs_np, orc)
@@ -211,7 +228,7 @@ def _random_case(orc, b, layers=2):
     pools = [torch.from_numpy(pool_np).cuda()]
     curs = [torch.from_numpy(cur_np).cuda()]
     r = _runner(b, pools, curs)
-    r.run(layers)
+    _run_poisoned(r, layers)
     torch.cuda.synchronize()
     want = _check_plan(b, r, orc)
     for layer in range(max(0, layers - 2), layers):
