@@ -203,7 +203,9 @@ int gpb_plan_build(const gpb_batch *batch, const gpb_plan *plan, void *stream);
  * commit "current rows written straight into staging": the fill writes into
  * the zeroed staging span).  The staging rows a batch writes are the same in
  * every layer, so one clear per batch serves all its layers.  A kernel, not a
- * memset node, so the call can be captured in a HIP graph. */
+ * memset node, so the call can be captured in a HIP graph.  Errors:
+ * GPB_EINVAL (n_bytes < 0, or d_ptr NULL with n_bytes > 0), GPB_EALIGN,
+ * GPB_ERANGE (more than 2^31 workgroups of 4 KiB), GPB_EHIP. */
 int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream);
 
 /* Per layer: staging row d_staging_rows[t] <- current row t, for t < n_rows,
@@ -214,7 +216,11 @@ int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream);
  * outside [0, n_staging_rows) is skipped and GPB_STATUS_BAD_STAGING_ROW is
  * ORed into *d_status when d_status is not NULL (page 0d87bc5: index_copy_
  * has no skip semantics for a stray -1, so the plan must never emit one).
- * Rows must not repeat (the plan's rows are distinct). */
+ * Rows must not repeat (the plan's rows are distinct), and the staging region
+ * must not overlap the current rows.  Errors: GPB_EINVAL (negative sizes,
+ * row_bytes < 1, a NULL pointer with n_rows > 0), GPB_EALIGN, GPB_ERANGE (the
+ * current rows or the staging region reach 2 GiB: each is one 32-bit buffer
+ * range), GPB_EHIP. */
 int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
                             const int32_t *d_staging_rows,
                             const void *d_cur_rows, int32_t n_rows,
@@ -227,7 +233,11 @@ int gpb_current_row_scatter(void *d_staging, int64_t n_staging_rows,
  * zero-filled (page d63fbd4, commit "compose_v2").  A descriptor with owner
  * >= table->n or src >= table->n_pages[owner] is zero-filled as well and
  * GPB_STATUS_BAD_DESCRIPTOR is ORed into *d_status when d_status is not NULL.
- * The dense buffer must not overlap any source page it reads. */
+ * The dense buffer must not overlap any source page it reads.  Errors:
+ * GPB_EINVAL (table NULL, table->n outside 1..GPB_MAX_SOURCES, a negative
+ * n_pages, a NULL base with pages, n_slots < 0, page_rows < 1, a NULL
+ * pointer with n_slots > 0), GPB_EALIGN, GPB_ERANGE (a page of 2 GiB - 1 MiB
+ * or more: each page is one 32-bit buffer range), GPB_EHIP. */
 int gpb_compose_gather(void *d_dense, const gpb_sources *table,
                        const int32_t *d_owner, const int32_t *d_src,
                        int32_t n_slots, int32_t page_rows, int32_t row_bytes,
@@ -239,7 +249,8 @@ int gpb_compose_gather(void *d_dense, const gpb_sources *table,
  * after the scatter); other slots of d_dense are not touched.  n_slots is the
  * number of slots d_dense, d_owner and d_src hold: a listed slot outside
  * [0, n_slots) is skipped and GPB_STATUS_BAD_DESCRIPTOR is ORed into
- * *d_status.  A slot must not be listed twice. */
+ * *d_status.  A slot must not be listed twice.  Errors as gpb_compose_gather,
+ * plus GPB_EINVAL for n_list < 0. */
 int gpb_compose_gather_slots(void *d_dense, const gpb_sources *table,
                              const int32_t *d_slots, int32_t n_list,
                              const int32_t *d_owner, const int32_t *d_src,
@@ -251,7 +262,9 @@ int gpb_compose_gather_slots(void *d_dense, const gpb_sources *table,
  * pool row d_pool_locs[t] of d_pool (its KV-cache location), whole rows of
  * row_bytes.  A destination outside [0, n_staging_rows) or [0, n_pool_rows)
  * is skipped there and GPB_STATUS_BAD_STAGING_ROW is ORed into *d_status.
- * The staging region is below 2 GiB; the pool may be any size. */
+ * The staging region is below 2 GiB; the pool may be any size.  Errors as
+ * gpb_current_row_scatter, plus GPB_EINVAL for n_pool_rows < 0 or a NULL pool
+ * or pool_locs with n_rows > 0. */
 int gpb_current_row_fill(void *d_staging, int64_t n_staging_rows,
                          const int32_t *d_staging_rows, void *d_pool,
                          int64_t n_pool_rows, const int32_t *d_pool_locs,
@@ -281,13 +294,17 @@ typedef struct gpb_gather_group {   /* one format's slot-dense gather      */
   int32_t row_bytes;                /* multiple of 16                     */
 } gpb_gather_group;
 
-/* gpb_current_row_scatter for every group, one launch. */
+/* gpb_current_row_scatter for every group, one launch.  Errors as
+ * gpb_current_row_scatter for any group, plus GPB_EINVAL for n_groups outside
+ * 1..GPB_MAX_GROUPS and GPB_ERANGE past 2^31 workgroups in total. */
 int gpb_current_row_scatter_groups(const gpb_row_group *groups, int32_t n_groups,
                                    const int32_t *d_staging_rows, int32_t n_rows,
                                    int32_t *d_status, void *stream);
 
 /* gpb_compose_gather for every group (same descriptors and page_rows), one
- * launch. */
+ * launch.  Errors as gpb_compose_gather for any group (a group's table holds
+ * at most GPB_MAX_GROUP_SOURCES entries), plus GPB_EINVAL for n_groups outside
+ * 1..GPB_MAX_GROUPS and GPB_ERANGE past 2^31 workgroups in total. */
 int gpb_compose_gather_groups(const gpb_gather_group *groups, int32_t n_groups,
                               const int32_t *d_owner, const int32_t *d_src,
                               int32_t n_slots, int32_t page_rows, int32_t *d_status,
