@@ -495,14 +495,15 @@ def test_batch_replays_in_a_hip_graph(orc):
 
 @pytest.mark.parametrize("seed", range(2))
 def test_grouped_formats_match_single_format(orc, seed):
-    """One scatter launch and one gather launch for two or three row formats
-    on one plan give, per format, the single-format result (the oracle's)."""
+    """One scatter launch and one gather launch for two to four row formats
+    (four, the most a launch takes, on the first batch) on one plan give, per
+    format, the single-format result (the oracle's)."""
     gpb = _gpb()
     rng = np.random.default_rng(900 + seed)
     for i in range(12):
         b = workloads.random_batch(rng, page_size=int(rng.choice([1, 4, 16, 64])))
-        sizes = [b.row_bytes] + [int(16 * rng.integers(1, 10))
-                                 for _ in range(int(rng.integers(1, 3)))]
+        extra = 3 if i == 0 else int(rng.integers(1, 4))
+        sizes = [b.row_bytes] + [int(16 * rng.integers(1, 10)) for _ in range(extra)]
         runners, host = [], []
         plan = None
         for k, rb in enumerate(sizes):
@@ -518,6 +519,8 @@ def test_grouped_formats_match_single_format(orc, seed):
             host.append((bk, pool_np, cur_np))
         for r in runners:
             r.begin_batch()
+            for d in r.dense:
+                d.fill_(POISON)
         for layer in range(2):
             gpb.layer_groups(runners, layer)
         torch.cuda.synchronize()
