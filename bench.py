@@ -44,6 +44,9 @@ def _args():
                     help="write profiles/ summaries from three rocprofv3 csv output "
                          "directories (kernel trace + stats, FETCH_SIZE, WRITE_SIZE) "
                          "and exit; runs on the host only")
+    ap.add_argument("--summarize-extras", metavar="TRACE",
+                    help="write profiles/compose_<workload>_extras_kernels.txt from the "
+                         "rocprofv3 kernel-trace directory of a default run and exit")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the headline path only (no prefetch split, fused fill "
                          "or twin): the mode the profiler runs use")
@@ -210,15 +213,21 @@ def _short(name):
     kept (they tell the gather from the slot-list gather, the scatter from the
     fused fill)."""
     import re
-    for key in ("k_compose_gather", "k_row_scatter", "k_fill_zero", "k_plan_scan_fill",
-                "k_plan_slots", "k_plan_tokens", "copyBuffer"):
+    for key in ("k_compose_gather", "k_row_scatter", "k_gather_groups", "k_scatter_groups",
+                "k_fill_zero", "k_plan_scan_fill", "k_plan_slots", "k_plan_tokens",
+                "copyBuffer"):
         if key in name:
             m = re.search(key + r"(<[^>]*>)?", name)
             return m.group(0).replace(" ", "")
     return name[:60]
 
 
-# $REPO is the repository root, $OUT the directory the three runs write to
+# $REPO is the repository root, $OUT the directory the runs write to
+EXTRAS_TRACE_COMMAND = (
+    "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
+    "-d $OUT/prof_extras -o extras -- python3 $REPO/bench.py "
+    "--steps 2 --warmup 1 --cpu-seconds 0")
+
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $OUT/prof_trace -o trace -- python3 $REPO/bench.py "
@@ -244,6 +253,32 @@ def _profile_commands(trace_dir, workload="traced"):
         v = v.replace("$OUT", "$REPO/" + out if k != "summary" else out)
         cmds[k] = (v + flag) if k == "summary" else v.replace("bench.py", "bench.py" + flag, 1)
     return cmds
+
+
+def summarize_extras(trace_dir, workload="traced"):
+    """profiles/compose_<workload>_extras_kernels.txt: kernel statistics of a
+    default bench run (headline path plus the prefetch split, fused fill,
+    index-key twin and grouped launches), trace only."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    out = os.path.relpath(os.path.dirname(os.path.abspath(trace_dir)), ROOT)
+    cmd = EXTRAS_TRACE_COMMAND.replace("$OUT", "$REPO/" + out)
+    if workload != "traced":
+        cmd = cmd.replace("bench.py", "bench.py --workload " + workload, 1)
+    lines = ["# rocprofv3 kernel statistics, %s workload with the extras "
+             "(bench.py default run)" % workload,
+             "# command: " + cmd,
+             "# LIST = slot-list gather (prefetch split), FILL = fused fill, "
+             "*_groups = token KV and index twin in one launch",
+             "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
+                                              "max_ns", "pct")]
+    for r in stats:
+        lines.append("%-34s %7s %12.0f %12.0f %12.0f %8.2f" % (
+            _short(r["Name"]), r["Calls"], float(r["AverageNs"]), float(r["MinNs"]),
+            float(r["MaxNs"]), float(r["Percentage"])))
+    path = os.path.join(ROOT, "profiles", "compose_%s_extras_kernels.txt" % workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
@@ -325,6 +360,9 @@ def main():
     a = _args()
     if a.summarize_profiles:
         summarize_profiles(*a.summarize_profiles, workload=a.workload)
+        return
+    if a.summarize_extras:
+        summarize_extras(a.summarize_extras, workload=a.workload)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU only: the compose path here has no "
