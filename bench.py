@@ -342,12 +342,17 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     return rec
 
 
-def _timed(stream, fn, reps):
+def _timed(stream, fn, reps, lead=None):
     """Average ms of ``fn`` over ``reps`` back-to-back calls, HIP events on
-    the launch stream around the whole region."""
+    the launch stream around the whole region.  ``lead`` enqueues GPU work
+    before the start event, long enough that the host has queued every call
+    before the GPU reaches it: the region then holds GPU time only, even for
+    calls whose host side is slower than their kernels."""
     import torch
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if lead is not None:
+        lead()
     start.record(stream)
     for _ in range(reps):
         fn()
@@ -407,9 +412,15 @@ def main():
     # per-kernel averages: each kernel alone, launched back to back with the
     # layer loop's arguments, K*L launches per region
     reps = a.steps
-    g_ms = _timed(stream, lambda: [runner.gather(l, stream) for l in range(L)], reps) / L
-    s_ms = _timed(stream, lambda: [runner.scatter(l, stream) for l in range(L)], reps) / L
-    p_ms = _timed(stream, lambda: runner.begin_batch(stream), reps)
+    lead = lambda: [runner.gather(l, stream) for l in range(L)]  # noqa: E731
+    g_ms = _timed(stream, lambda: [runner.gather(l, stream) for l in range(L)], reps,
+                  lead=lead) / L
+    s_ms = _timed(stream, lambda: [runner.scatter(l, stream) for l in range(L)], reps,
+                  lead=lead) / L
+    # plan build + clear: host validation and four launches take longer on the
+    # host than their kernels on the GPU, so a lead of gathers keeps the GPU
+    # busy while the calls are queued
+    p_ms = _timed(stream, lambda: runner.begin_batch(stream), reps, lead=lead)
     # host time of one gpb_plan_build call (validation + three launches, no
     # synchronisation), for comparison with host-side plan builders
     torch.cuda.synchronize()
