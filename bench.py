@@ -470,11 +470,13 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
     import torch
     import gather_plan_build_amd as gpb
     import workloads
+    lead = lambda: [runner.gather(l, stream) for l in range(L)]  # noqa: E731
     pre_ms = _timed(stream, lambda: [runner.gather_prefix(l, stream) for l in range(L)],
-                    reps) / L
+                    reps, lead=lead) / L
     cur_ms = _timed(stream, lambda: [runner.gather_current(l, stream) for l in range(L)],
-                    reps) / L
-    fill_ms = _timed(stream, lambda: [runner.fill(l, stream) for l in range(L)], reps) / L
+                    reps, lead=lead) / L
+    fill_ms = _timed(stream, lambda: [runner.fill(l, stream) for l in range(L)], reps,
+                     lead=lead) / L
     # the whole step captured once as a HIP graph and replayed: same kernels,
     # no per-launch host work
     side = torch.cuda.Stream()
@@ -484,7 +486,7 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
         runner.run(L, side)
     torch.cuda.synchronize()
     graph.replay()
-    graph_ms = _timed(stream, graph.replay, reps)
+    graph_ms = _timed(stream, graph.replay, reps, lead=lead)
     out["graph_replay"] = {"ms_per_step": round(graph_ms, 4),
                            "us_per_layer_incl_plan": round(graph_ms * 1e3 / L, 2)}
     del graph
@@ -506,12 +508,13 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
                           batch.prefix_pages, batch.cur_tokens, batch.req_pages),
             ipools, icurs, plan=runner.plan)
         twin.begin_batch(stream)
-        t_ms = _timed(stream, lambda: [twin.layer(l, stream) for l in range(L)], reps) / L
+        t_ms = _timed(stream, lambda: [twin.layer(l, stream) for l in range(L)], reps,
+                      lead=lead) / L
         tb = twin.algorithmic_bytes_per_layer()
         sep_ms = _timed(stream, lambda: [(runner.layer(l, stream), twin.layer(l, stream))
-                                         for l in range(L)], reps) / L
+                                         for l in range(L)], reps, lead=lead) / L
         both_ms = _timed(stream, lambda: [gpb.layer_groups([runner, twin], l, stream)
-                                          for l in range(L)], reps) / L
+                                          for l in range(L)], reps, lead=lead) / L
         both_b = runner.algorithmic_bytes_per_layer() + tb
         out["index_twin"] = {"row_bytes": rb, "us_per_layer": round(t_ms * 1e3, 2),
                              "algorithmic_bytes_per_layer": tb,
