@@ -3,8 +3,10 @@
 Each case rewrites one line of oracle/gpb_oracle.c (a dropped term, a wrong
 index or bound, an inclusive instead of exclusive sum, a missing zero fill),
 builds the variant with gcc in a temporary directory and runs every pin of
-tests/pins.py against it in a child process.  The child must fail.  This is
-CPU-only and never touches the product library."""
+tests/pins.py against it in a child process.  The child must fail.  The
+numpy closed form, the oracle's second route, gets the same treatment: a
+child process replaces it with a rewritten copy before running the pins.
+This is CPU-only and never touches the product library."""
 import os
 import subprocess
 import sys
@@ -131,6 +133,56 @@ def test_planted_mistake_is_caught(name):
                            text=True, timeout=300)
     assert r.returncode in (3, 4), "planted mistake %s was not caught by a pin (rc %d):\n%s" % (
         name, r.returncode, r.stdout[-2000:] + r.stderr[-2000:])
+
+
+CLOSED_FORM = os.path.join(ROOT, "oracle", "closed_form.py")
+
+CLOSED_FORM_MUTANTS = {
+    "cf_page_cursor_skips_current": ("page_cursor += P + C", "page_cursor += P"),
+    "cf_tail_not_zero": ("block = np.zeros((C * PS, RB), dtype=np.uint8)",
+                         "block = np.ones((C * PS, RB), dtype=np.uint8)"),
+    "cf_token_cursor_frozen": ("token_cursor += c", "token_cursor += 0"),
+    "cf_pool_page_not_scaled": ("pool_rows[page * PS:(page + 1) * PS]",
+                                "pool_rows[page:page + PS]"),
+    "cf_prefix_page_offset": ("int(req_pages[page_cursor + k])",
+                              "int(req_pages[page_cursor + k + 1 if k + 1 < P else k])"),
+}
+
+CF_CHILD = r"""
+import os, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, pins
+from oracle import closed_form
+src = open({path!r}).read()
+assert src.count({old!r}) >= 1, "mutation target not found"
+exec(compile(src.replace({old!r}, {new!r}, 1), {path!r}, "exec"), closed_form.__dict__)
+try:
+    pins.run_all(oracle.default(), n_random=40)
+except AssertionError as e:
+    print("PIN FAILED:", e, flush=True)
+    os._exit(3)
+print("ALL PINS PASSED")
+"""
+
+
+@pytest.mark.parametrize("name", sorted(CLOSED_FORM_MUTANTS))
+def test_planted_closed_form_mistake_is_caught(name):
+    old, new = CLOSED_FORM_MUTANTS[name]
+    code = CF_CHILD.format(root=ROOT, tests=HERE, path=CLOSED_FORM, old=old, new=new)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 3, "planted mistake %s was not caught by a pin (rc %d):\n%s" % (
+        name, r.returncode, r.stdout[-2000:] + r.stderr[-2000:])
+
+
+def test_unmutated_closed_form_passes_in_child():
+    """Control for the mechanism above: the same re-exec with nothing changed
+    passes every pin."""
+    old = CLOSED_FORM_MUTANTS["cf_token_cursor_frozen"][0]
+    code = CF_CHILD.format(root=ROOT, tests=HERE, path=CLOSED_FORM, old=old, new=old)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0 and "ALL PINS PASSED" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]
 
 
 def test_unmutated_oracle_passes_in_child():
