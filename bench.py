@@ -99,13 +99,23 @@ def _host_threads():
 
 
 def cpu_baseline(batch, pools, curs, budget_s, threads=None):
-    """The CPU oracle (plain C loops) on the same batch: the plan once, then
-    layers until the budget is spent, first on one thread, then as
-    ``threads`` concurrent copies of the same single-threaded oracle (each
-    with its own staging and dense buffers, layers dealt round-robin) for
-    half the budget.  Returns the JSON object; its headline is the
-    single-threaded figure, the concurrent one sits under "threaded"."""
+    """The CPU oracle (plain C loops) on the same batch, the plan built once:
+
+    - headline: layers on one thread until the budget is spent (median per
+      layer);
+    - "threaded": one layer at a time on ``threads`` threads, split as
+      contiguous slot ranges: the staging zero and the row scatter on one
+      thread (the oracle's layer with no slots), then the gather as one
+      contiguous range of dense slots per thread (the oracle's slot-list
+      gather), a quarter of the budget;
+    - "concurrent_layers": ``threads`` copies of the single-threaded oracle
+      running different layers at once, each with its own staging and dense
+      buffers, a quarter of the budget (host throughput, not latency).
+
+    The oracle itself is the same in all three; only how its calls are spread
+    over threads differs."""
     import threading
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
     orc = oracle.default()
@@ -116,12 +126,13 @@ def cpu_baseline(batch, pools, curs, budget_s, threads=None):
     for k in range(min(len(pools), batch.n_layers)):
         host_pools[k] = pools[k].cpu().numpy().reshape(-1)
         host_curs[k] = curs[k].cpu().numpy()
+    PS, RB = batch.page_size, batch.row_bytes
 
     def run_layer(layer, staging):
         k = layer % len(pools)
-        oracle.layer_for(batch, want, host_pools[k], host_curs[k], staging, orc)
+        return oracle.layer_for(batch, want, host_pools[k], host_curs[k], staging, orc)
 
-    staging = np.empty(batch.staging_rows_total * batch.row_bytes, np.uint8)
+    staging = np.empty(batch.staging_rows_total * RB, np.uint8)
     per_layer = []
     spent = 0.0
     runs = 0
@@ -135,7 +146,6 @@ def cpu_baseline(batch, pools, curs, budget_s, threads=None):
         spent += dt
         runs += 1
     S, T = batch.n_req_pages, batch.n_cur_tokens
-    PS, RB = batch.page_size, batch.row_bytes
     layer_bytes = (2 * S * PS * RB + 2 * T * RB + 8 * S + 4 * T
                    + 8 * (batch.n_pool_entries + batch.n_writers))
     med = sorted(per_layer)[len(per_layer) // 2]
@@ -150,39 +160,80 @@ def cpu_baseline(batch, pools, curs, budget_s, threads=None):
            "cpu_model": _cpu_model(), "host_threads_available": os.cpu_count()}
 
     n = threads if threads is not None else _host_threads()
-    if n > 1:
-        # the oracle's C calls release the GIL (ctypes), so the copies run
-        # concurrently; all start together and run for the same wall time
-        done = [0] * n
-        seconds = max(budget_s / 2, 1e-3)
-        barrier = threading.Barrier(n + 1)
+    if n <= 1:
+        return out
 
-        def worker(w):
-            st = np.empty(batch.staging_rows_total * batch.row_bytes, np.uint8)
-            run_layer(w % batch.n_layers, st)  # untimed: first touch of its buffers
-            barrier.wait()
-            deadline = time.perf_counter() + seconds
-            layer = w
-            while time.perf_counter() < deadline:
-                run_layer(layer % batch.n_layers, st)
-                done[w] += 1
-                layer += n
+    # one layer on n threads, split by contiguous slot ranges
+    bounds = np.linspace(0, S, n + 1).astype(np.int64)
+    ranges = [np.arange(bounds[i], bounds[i + 1], dtype=np.int32) for i in range(n)]
+    dense = np.empty((S * PS, RB), np.uint8)
+    no_slots = want["owner"][:0]
 
-        pool = [threading.Thread(target=worker, args=(w,)) for w in range(n)]
-        for t in pool:
-            t.start()
+    def split_layer(pool_exec, layer):
+        k = layer % len(pools)
+        table = oracle.pointer_table(host_pools[k], staging, batch.n_pool_entries,
+                                     batch.n_writers, batch.staging_cap_pages, PS, RB)
+        orc.compose_layer(table, host_curs[k], want["staging_rows"], no_slots, no_slots,
+                          PS, RB, staging)  # staging zero + scatter only
+        list(pool_exec.map(lambda sl: orc.gather_slots(table, sl, want["owner"], want["src"],
+                                                       PS, RB, dense), ranges))
+
+    with ThreadPoolExecutor(n) as ex:
+        split_layer(ex, 0)  # untimed: first touch; also checked against the one-thread layer
+        ref, _ = run_layer(0, np.empty_like(staging))
+        if not np.array_equal(ref, dense):
+            raise AssertionError("slot-range split of the oracle differs from the oracle")
+        del ref
+        split = []
+        spent = 0.0
+        while spent < budget_s / 4 or len(split) < 3:
+            t0 = time.perf_counter()
+            split_layer(ex, len(split) % batch.n_layers)
+            dt = time.perf_counter() - t0
+            split.append(dt)
+            spent += dt
+    med_split = sorted(split)[len(split) // 2]
+    out["threaded"] = {
+        "value": round(layer_bytes / med_split / 1e9, 3), "unit": "GB/s", "cores": n,
+        "kind": "oracle", "us_per_layer": round(med_split * 1e6, 1),
+        "sample": "%d layer runs, median per layer; staging zero and row scatter on one "
+                  "thread, then the gather as %d contiguous slot ranges on %d threads"
+                  % (len(split), n, n)}
+    del dense
+
+    # n single-threaded oracles on different layers at once
+    done = [0] * n
+    seconds = max(budget_s / 4, 1e-3)
+    barrier = threading.Barrier(n + 1)
+
+    def worker(w):
+        st = np.empty(batch.staging_rows_total * RB, np.uint8)
+        run_layer(w % batch.n_layers, st)  # untimed: first touch of its buffers
         barrier.wait()
-        t0 = time.perf_counter()
-        for t in pool:
-            t.join()
-        wall = time.perf_counter() - t0
-        total = sum(done)
-        out["threaded"] = {
-            "value": round(layer_bytes * total / wall / 1e9, 3), "unit": "GB/s",
-            "cores": n, "kind": "oracle",
-            "sample": "%d layer runs over %.1f s wall on %d threads, each a copy of "
-                      "the single-threaded oracle with its own staging and dense "
-                      "buffers" % (total, wall, n)}
+        deadline = time.perf_counter() + seconds
+        layer = w
+        while time.perf_counter() < deadline:
+            run_layer(layer % batch.n_layers, st)
+            done[w] += 1
+            layer += n
+
+    # the oracle's C calls release the GIL (ctypes), so the copies run
+    # concurrently; all start together and run for the same wall time
+    workers = [threading.Thread(target=worker, args=(w,)) for w in range(n)]
+    for t in workers:
+        t.start()
+    barrier.wait()
+    t0 = time.perf_counter()
+    for t in workers:
+        t.join()
+    wall = time.perf_counter() - t0
+    total = sum(done)
+    out["concurrent_layers"] = {
+        "value": round(layer_bytes * total / wall / 1e9, 3), "unit": "GB/s",
+        "cores": n, "kind": "oracle",
+        "sample": "%d layer runs over %.1f s wall on %d threads, each a copy of "
+                  "the single-threaded oracle with its own staging and dense "
+                  "buffers" % (total, wall, n)}
     return out
 
 
