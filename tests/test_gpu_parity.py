@@ -274,6 +274,51 @@ def test_row_and_page_geometry(orc, ps, rb):
         _random_case(orc, b)
 
 
+def test_two_host_threads_on_two_streams(orc):
+    """The library keeps no global state: two host threads, each driving its
+    own batch on its own stream (default priority), interleave their plan
+    builds, clears, scatters and gathers, and both results match the
+    oracle."""
+    import threading
+    rng = np.random.default_rng(77)
+    batches = [workloads.random_batch(rng, max_bs=8, max_pool=200, page_size=16,
+                                      row_bytes=1152) for _ in range(2)]
+    cases = []
+    for b in batches:
+        pool_np, cur_np = pins.tagged_values(b)
+        r = _runner(b, [torch.from_numpy(pool_np).cuda()], [torch.from_numpy(cur_np).cuda()])
+        cases.append((b, r, pool_np, cur_np, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def drive(case):
+        b, r, _, _, st = case
+        try:
+            with torch.cuda.stream(st):
+                for it in range(3):
+                    r.begin_batch(st)
+                    for layer in range(4):
+                        if it == 2 and layer >= 2:
+                            r.dense[layer % 2].fill_(POISON)
+                        r.layer(layer, st)
+            st.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=drive, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for b, r, pool_np, cur_np, _ in cases:
+        want = _check_plan(b, r, orc)
+        for layer in (2, 3):
+            _check_layer(b, r, layer, want, [pool_np], [cur_np], orc)
+        assert _status(r) == 0
+
+
 def _full_table_batch():
     """The largest pointer table the ABI takes: 32 pool entries and 32 staging
     slabs (64 entries), with 51 current pages dealt round robin over the 32
