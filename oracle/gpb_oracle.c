@@ -21,6 +21,19 @@
  * Every value is an integer; rows are opaque byte strings.  All loops are
  * the plainest form of the step they implement; nothing is fused, blocked
  * or reordered.
+ *
+ * Parity status (the pins live in tests/):
+ *   gpbo_validate, gpbo_counts, gpbo_plan's spans, slot pages, page inverse,
+ *   staging page inverse, owner/src, writer, staging rows and mixed_locs,
+ *   gpbo_layer, gpbo_gather_slots, gpbo_fill, gpbo_prefetch_lists and the
+ *   token_req of gpbo_token_expansions: pinned (brute force on tagged rows,
+ *   the closed form, torch index_copy_ / index_select and numpy take and
+ *   repeat, a hand-derived worked example).
+ *   q_lens, kv_lens, q_starts, k_bases, current_bases, q_bases, and the
+ *   topk_offsets and segments of gpbo_token_expansions: the pages give only
+ *   their names, so they are pinned only to their stated definitions through
+ *   the dense and staging geometry they must agree with -- parity unpinned as
+ *   far as the pages themselves go.
  */
 #include <stdint.h>
 #include <stdlib.h>
