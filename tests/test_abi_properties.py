@@ -1,0 +1,68 @@
+"""Property-based agreement of the library's host validation with the
+oracle's (hypothesis): batches drawn with several faults at once -- negative
+or zero geometry, negative counts, row sizes off the 16-byte grid, page ids
+0, repeated or past the pool, staging capacity short by one, geometry whose
+rows overflow int32 -- must be accepted or rejected by both for the same
+reason, and when accepted give the same S, T and NCP.  Host only."""
+import ctypes
+
+import numpy as np
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import oracle
+from gather_plan_build_amd import binding as B
+
+_CODE_OF = {oracle.OK: {B.OK}, oracle.BAD_SHAPE: {B.EINVAL, B.EALIGN},
+            oracle.BAD_PAGE: {B.EPAGE}, oracle.CAPACITY: {B.ECAPACITY},
+            oracle.TOO_LARGE: {B.ERANGE}}
+
+
+@st.composite
+def batches(draw):
+    # mostly well-formed geometry, each field occasionally broken, so every
+    # outcome (accepted, bad shape, bad page, capacity, int32 overflow) occurs
+    bs = draw(st.sampled_from([0, 1, 2, 3, 4, 5, 6, 3, 4, 5, 6, -1]))
+    ps = draw(st.sampled_from([1, 3, 16, 64, 64, 16, 1 << 20, 1 << 20, 0]))
+    rb = draw(st.sampled_from([16, 48, 656, 1152, 1152, 656, 48, 16, 8, 0, 1160]))
+    npp = draw(st.sampled_from([40, 60, 200, 40, 60, 200, 5000, 5000, 1]))
+    np_ = draw(st.sampled_from([1, 1, 2, 3, 1, 2, 0]))
+    w = draw(st.sampled_from([1, 1, 2, 3, 1, 2, 0]))
+    n = max(bs, 0)
+    P = [draw(st.sampled_from([0, 1, 2, 3, 4, 0, 1, 2, -1])) for _ in range(n)]
+    cmax = 3 * max(ps, 1) if ps < 1024 else 5
+    c = [draw(st.one_of(st.integers(0, cmax), st.just(-1) if draw(st.integers(0, 9)) == 0
+                        else st.integers(0, cmax))) for _ in range(n)]
+    # exactly as many page ids as the counts describe (when they describe any)
+    if ps >= 1 and all(x >= 0 for x in P + c):
+        need = sum(P) + sum(-(-x // ps) for x in c)
+        ncp = sum(-(-x // ps) for x in c)
+    else:
+        need, ncp = 0, 0
+    rng = np.random.default_rng(draw(st.integers(0, 2 ** 32 - 1)))
+    pages = [int(x) for x in rng.choice(np.arange(1, max(npp, need + 2)), need, replace=False)]
+    fault = draw(st.sampled_from(["none", "none", "none", "zero", "dup", "past", "neg"]))
+    if need and fault == "zero":
+        pages[draw(st.integers(0, need - 1))] = 0
+    elif need > 1 and fault == "dup":
+        pages[-1] = pages[0]
+    elif need and fault == "past":
+        pages[draw(st.integers(0, need - 1))] = npp
+    elif need and fault == "neg":
+        pages[0] = -1
+    cap = max(0, 1 + ncp + draw(st.sampled_from([0, 1, 2, 0, 1, -1])))
+    return bs, ps, rb, npp, np_, w, cap, P, c, pages
+
+
+@settings(max_examples=600, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(batches())
+def test_host_validation_agrees_with_the_oracle(b):
+    bs, ps, rb, npp, np_, w, cap, P, c, pages = b
+    orc = oracle.default()
+    want = orc.validate(bs, ps, rb, npp, np_, w, cap, P, c, pages)
+    m = B.BatchMeta(bs, ps, rb, npp, np_, w, cap, P, c, pages)
+    S, T, NCP = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(-1)
+    got = B.lib.gpb_plan_sizes(ctypes.byref(m.c), ctypes.byref(S), ctypes.byref(T),
+                               ctypes.byref(NCP))
+    assert got in _CODE_OF[want], (want, got, b)
+    if want == oracle.OK:
+        assert (S.value, T.value, NCP.value) == tuple(orc.counts(bs, ps, P, c)), b
