@@ -7,6 +7,7 @@ bytes the GPU reads."""
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, given, settings, strategies as st
 
 import oracle
 import pins
@@ -317,6 +318,35 @@ def test_two_host_threads_on_two_streams(orc):
         for layer in (2, 3):
             _check_layer(b, r, layer, want, [pool_np], [cur_np], orc)
         assert _status(r) == 0
+
+
+@st.composite
+def _valid_batches(draw):
+    """Well-formed small batches of every geometry the kernels distinguish:
+    row sizes on both sides of the scalar-row threshold (21 chunks), pages of
+    1 to 64 rows, 1 to 4 pool entries and writers, spare staging pages."""
+    ps = draw(st.sampled_from([1, 2, 4, 16, 64]))
+    rb = draw(st.sampled_from([16, 48, 144, 320, 336, 656, 1152]))
+    bs = draw(st.integers(0, 8))
+    P = np.array([draw(st.integers(0, 4)) for _ in range(bs)], np.int32)
+    c = np.array([draw(st.integers(0, 3 * ps)) for _ in range(bs)], np.int32)
+    need = int(P.sum() + ((c + ps - 1) // ps).sum())
+    n_pool = need + 1 + draw(st.integers(0, 20))
+    rng = np.random.default_rng(draw(st.integers(0, 2 ** 32 - 1)))
+    pages = rng.choice(np.arange(1, n_pool), need, replace=False).astype(np.int32)
+    np_, w = draw(st.integers(1, 4)), draw(st.integers(1, 4))
+    cap = workloads.staging_cap_for(int(c.sum()), bs, ps) + draw(st.integers(0, 2))
+    return workloads.Batch("hypothesis", bs, ps, rb, n_pool, np_, w, cap, P, c, pages)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(_valid_batches())
+def test_property_random_batches_byte_exact(orc, b):
+    """Hypothesis-drawn batches (fixed derivation, so every run draws the
+    same ones): plan, two layers and both prefetch-split variants byte-exact
+    against the oracle."""
+    _random_case(orc, b)
 
 
 def _full_table_batch():
