@@ -79,6 +79,102 @@ static int32_t rd32(FILE *f) {
   return v;
 }
 
+/* Equality of two device regions, compared on the host. */
+static int same_device_bytes(const void *a, const void *b, size_t n) {
+  if (n == 0) return 1;
+  uint8_t *ha = malloc(n), *hb = malloc(n);
+  int ok = ha && hb && hipMemcpy(ha, a, n, hipMemcpyDeviceToHost) == hipSuccess &&
+           hipMemcpy(hb, b, n, hipMemcpyDeviceToHost) == hipSuccess && memcmp(ha, hb, n) == 0;
+  free(ha);
+  free(hb);
+  return ok;
+}
+
+/* The remaining entry points against the layer just composed by the core
+ * calls: the prefetch split (prefix slots, then current slots) and the
+ * grouped gather must reproduce its dense buffer; the grouped scatter and the
+ * fused fill must reproduce its staging, and the fill must leave each current
+ * row at its pool row and every other pool byte as it was. */
+static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_sources *t,
+                              int32_t S, int32_t T, int32_t NCP, void *d_pool, void *d_cur,
+                              void *d_stag, void *d_dense, const uint8_t *h_pool,
+                              const uint8_t *h_cur, int32_t *d_status, hipStream_t st) {
+  const size_t RB = (size_t)b->row_bytes, PS = (size_t)b->page_size;
+  const size_t dense_bytes = (size_t)S * PS * RB;
+  const size_t stag_rows = (size_t)b->n_writers * b->staging_cap_pages * PS;
+  const size_t pool_bytes = (size_t)b->n_pool_pages * PS * RB;
+  void *d_dense2, *d_stag2, *d_pool2;
+  HCHECK(hipMalloc(&d_dense2, dense_bytes + 16));
+  HCHECK(hipMalloc(&d_stag2, stag_rows * RB));
+  HCHECK(hipMalloc(&d_pool2, pool_bytes));
+
+  /* prefetch split: prefix slots a layer ahead, then the current slots */
+  HCHECK(hipMemset(d_dense2, 0xEE, dense_bytes + 16));
+  CHECK(gpb_compose_gather_slots(d_dense2, t, p->d_prefix_slots, S - NCP, p->d_owner,
+                                 p->d_src, S, b->page_size, b->row_bytes, d_status, st));
+  CHECK(gpb_compose_gather_slots(d_dense2, t, p->d_current_slots, NCP, p->d_owner,
+                                 p->d_src, S, b->page_size, b->row_bytes, d_status, st));
+  HCHECK(hipStreamSynchronize(st));
+  if (!same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+    fprintf(stderr, "prefetch split differs from the one-shot gather\n");
+    return 6;
+  }
+
+  /* grouped calls with one group each (the table fits a group's limit) */
+  if (t->n <= GPB_MAX_GROUP_SOURCES) {
+    CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
+    gpb_row_group rg = {d_stag2, (int64_t)stag_rows, d_cur, b->row_bytes};
+    CHECK(gpb_current_row_scatter_groups(&rg, 1, p->d_staging_rows, T, d_status, st));
+    HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
+    gpb_gather_group gg = {d_dense2, t, b->row_bytes};
+    CHECK(gpb_compose_gather_groups(&gg, 1, p->d_owner, p->d_src, S, b->page_size, d_status,
+                                    st));
+    HCHECK(hipStreamSynchronize(st));
+    if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB) ||
+        !same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+      fprintf(stderr, "grouped calls differ from the single-format calls\n");
+      return 7;
+    }
+  }
+
+  /* fused fill into a copy of the pool */
+  HCHECK(hipMemcpy(d_pool2, d_pool, pool_bytes, hipMemcpyDeviceToDevice));
+  CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
+  CHECK(gpb_current_row_fill(d_stag2, (int64_t)stag_rows, p->d_staging_rows, d_pool2,
+                             (int64_t)(b->n_pool_pages * PS), p->d_pool_locs, d_cur, T,
+                             b->row_bytes, d_status, st));
+  HCHECK(hipStreamSynchronize(st));
+  if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB)) {
+    fprintf(stderr, "fused fill staging differs from the scatter\n");
+    return 8;
+  }
+  int32_t *locs = malloc(4 * (size_t)T + 4);
+  uint8_t *want = malloc(pool_bytes), *got = malloc(pool_bytes);
+  HCHECK(hipMemcpy(locs, p->d_pool_locs, 4 * (size_t)T, hipMemcpyDeviceToHost));
+  HCHECK(hipMemcpy(got, d_pool2, pool_bytes, hipMemcpyDeviceToHost));
+  memcpy(want, h_pool, pool_bytes);
+  for (int32_t k = 0; k < T; k++) {
+    if (locs[k] < 0 || (size_t)locs[k] >= (size_t)b->n_pool_pages * PS) return 9;
+    memcpy(want + (size_t)locs[k] * RB, h_cur + (size_t)k * RB, RB);
+  }
+  int pool_ok = memcmp(want, got, pool_bytes) == 0;
+  free(locs);
+  free(want);
+  free(got);
+  if (!pool_ok) {
+    fprintf(stderr, "fused fill pool differs\n");
+    return 9;
+  }
+  int32_t status = -1;
+  HCHECK(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
+  if (status != 0) { fprintf(stderr, "status %d after the other entry points\n", status); return 5; }
+  HCHECK(hipFree(d_dense2));
+  HCHECK(hipFree(d_stag2));
+  HCHECK(hipFree(d_pool2));
+  printf("c consumer: slot-list gather, grouped calls and fused fill agree\n");
+  return 0;
+}
+
 static int run(const char *in, const char *out) {
   FILE *f = fopen(in, "rb");
   if (!f) return 4;
@@ -165,6 +261,9 @@ static int run(const char *in, const char *out) {
   int32_t status = -1;
   HCHECK(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
   if (status != 0) { fprintf(stderr, "status %d\n", status); return 5; }
+  int rc = other_entry_points(&b, &p, &t, S, T, NCP, d_pool, d_cur, d_stag, d_dense,
+                              h_pool, h_cur, d_status, st);
+  if (rc) return rc;
 
   FILE *o = fopen(out, "wb");
   if (!o) return 4;

@@ -86,6 +86,7 @@ def test_c_consumer_layer_matches_oracle(orc, seed):
             r = subprocess.run([exe, "run", fin, fout], capture_output=True, text=True,
                                timeout=120)
             assert r.returncode == 0, r.stdout + r.stderr
+            assert "slot-list gather, grouped calls and fused fill agree" in r.stdout, r.stdout
             plan, staging, dense = _read_result(fout, b)
             want = oracle.plan_for(b, orc)
             for name in oracle.PLAN_FIELDS:
