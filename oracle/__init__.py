@@ -31,8 +31,11 @@ Parity status per function (pins in tests/test_oracle_pins.py):
   closed form, library special cases, hand-derived worked example);
   token_req -- pinned to numpy repeat (the repeat_interleave the pages used);
   prefix_slots, current_slots, pool_locs, cur_page_token0, cur_page_ntok,
-  gather_slots, fill -- pinned by brute force on tagged rows and against the
-  full gather;
+  prefix_desc, current_desc, gather_slots, gather_records, fill -- pinned by
+  brute force on tagged rows and against the full gather;
+  writer_offsets, writer_tokens, writer_rows, writer_page_row0 -- pinned by
+  brute force: one torch index_copy_ per writer into its own slab rebuilds
+  the staging the single scatter writes, every token in exactly one list;
   q_lens, kv_lens, q_starts, k_bases, current_bases, q_bases, topk_offsets,
   segments -- the pages give only their names; pinned to the stated
   definitions through the dense and staging geometry they must agree with;
@@ -55,10 +58,12 @@ PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
                "owner", "src", "page_inverse", "staging_page_inverse", "writer",
                "staging_rows", "mixed_locs", "token_req", "topk_offsets", "segments",
                "prefix_slots", "current_slots", "pool_locs", "cur_page_token0",
-               "cur_page_ntok")
+               "cur_page_ntok", "prefix_desc", "current_desc", "writer_offsets",
+               "writer_tokens", "writer_rows", "writer_page_row0")
 # the arrays gpbo_plan writes; the next three come from gpbo_token_expansions,
-# the last five from gpbo_prefetch_lists
-_PLAN_CORE = PLAN_FIELDS[:-8]
+# the next five from gpbo_prefetch_lists, the two records from
+# gpbo_page_records and the last four from gpbo_writer_lists
+_PLAN_CORE = PLAN_FIELDS[:-14]
 
 
 def _i32(a):
@@ -84,6 +89,9 @@ class Oracle:
         lib.gpbo_prefetch_lists.restype = None
         lib.gpbo_gather_slots.restype = ctypes.c_int
         lib.gpbo_fill.restype = ctypes.c_int
+        lib.gpbo_page_records.restype = None
+        lib.gpbo_gather_records.restype = ctypes.c_int
+        lib.gpbo_writer_lists.restype = None
         self.lib = lib
         self.path = lib_path
 
@@ -134,7 +142,9 @@ class Oracle:
                  "staging_rows": T, "mixed_locs": T, "token_req": T,
                  "topk_offsets": T, "segments": 4 * bs, "prefix_slots": S - NCP,
                  "current_slots": NCP, "pool_locs": T, "cur_page_token0": NCP,
-                 "cur_page_ntok": NCP}
+                 "cur_page_ntok": NCP, "prefix_desc": 4 * (S - NCP),
+                 "current_desc": 4 * NCP, "writer_offsets": n_writers + 1,
+                 "writer_tokens": T, "writer_rows": T, "writer_page_row0": NCP}
         # -7 marks entries the oracle never wrote; each array carries a guard
         # tail as long as itself that must stay untouched
         out = {k: np.full(2 * sizes[k] + 64, -7, dtype=np.int32) for k in PLAN_FIELDS}
@@ -157,6 +167,15 @@ class Oracle:
                                      out["pool_locs"].ctypes.data_as(_I32P),
                                      out["cur_page_token0"].ctypes.data_as(_I32P),
                                      out["cur_page_ntok"].ctypes.data_as(_I32P))
+        P_ = lambda k: out[k].ctypes.data_as(_I32P)  # noqa: E731
+        self.lib.gpbo_page_records(P_("prefix_slots"), S - NCP, P_("owner"), P_("src"),
+                                   P_("prefix_desc"))
+        self.lib.gpbo_page_records(P_("current_slots"), NCP, P_("owner"), P_("src"),
+                                   P_("current_desc"))
+        self.lib.gpbo_writer_lists(bs, page_size, n_writers, staging_cap_pages, pP, pc,
+                                   P_("staging_rows"), P_("writer_offsets"),
+                                   P_("writer_tokens"), P_("writer_rows"),
+                                   P_("writer_page_row0"))
         for k in PLAN_FIELDS:
             assert np.all(out[k][sizes[k]:] == -7), "oracle wrote past " + k
         return {k: out[k][:sizes[k]].copy() for k in PLAN_FIELDS}
@@ -207,6 +226,23 @@ class Oracle:
                                 and dense.size >= len(ow) * page_size * RB)
         return bool(self.lib.gpbo_gather_slots(ptrs, pages, len(table), psl, len(sl),
                                                pow_, psc, page_size, RB, _p(dense)))
+
+    def gather_records(self, table, records, page_size, row_bytes, dense):
+        """O17: gather the pages named by (slot, owner, src, 0) records into
+        ``dense`` (uint8 [S*PS, RB]), leaving the other slots.  Returns the
+        out-of-range flag."""
+        RB = int(row_bytes)
+        assert dense.dtype == np.uint8 and dense.flags.c_contiguous
+        n_tab = max(len(table), 1)
+        ptrs = (ctypes.c_void_p * n_tab)(*[t.ctypes.data for t in table])
+        pages = (ctypes.c_int64 * n_tab)(*[t.size // (page_size * RB) for t in table])
+        rec, prec = _i32(records)
+        assert rec.size % 4 == 0
+        n = rec.size // 4
+        assert n == 0 or (rec[0::4].min() >= 0
+                          and (rec[0::4].max() + 1) * page_size * RB <= dense.size)
+        return bool(self.lib.gpbo_gather_records(ptrs, pages, len(table), prec, n,
+                                                 page_size, RB, _p(dense)))
 
     def fill(self, staging, staging_rows, pool, pool_locs, cur, row_bytes):
         """O15: each current row to its staging row and its pool row (uint8

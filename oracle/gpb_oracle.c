@@ -25,7 +25,8 @@
  * Parity status (the pins live in tests/):
  *   gpbo_validate, gpbo_counts, gpbo_plan's spans, slot pages, page inverse,
  *   staging page inverse, owner/src, writer, staging rows and mixed_locs,
- *   gpbo_layer, gpbo_gather_slots, gpbo_fill, gpbo_prefetch_lists and the
+ *   gpbo_layer, gpbo_gather_slots, gpbo_fill, gpbo_prefetch_lists,
+ *   gpbo_page_records, gpbo_gather_records, gpbo_writer_lists and the
  *   token_req of gpbo_token_expansions: pinned (brute force on tagged rows,
  *   the closed form, torch index_copy_ / index_select and numpy take and
  *   repeat, a hand-derived worked example).
@@ -375,4 +376,93 @@ int gpbo_fill(uint8_t *staging, int64_t n_staging_rows, const int32_t *staging_r
     else memcpy(pool + q * RB, row, (size_t)RB);
   }
   return bad;
+}
+
+/*
+ * O16: gather records for a list of dense slots (the two halves of the
+ * layer-ahead split, page 0d87bc5, commit "prefetch staging exchange"):
+ * record k is four int32 (slot, owner[slot], src[slot], 0), so a gather over
+ * the list finds everything about a page in one record.
+ */
+void gpbo_page_records(const int32_t *slots, int32_t n, const int32_t *owner,
+                       const int32_t *src, int32_t *records) {
+  for (int32_t k = 0; k < n; k++) {
+    int32_t s = slots[k];
+    records[4 * k + 0] = s;
+    records[4 * k + 1] = owner[s];
+    records[4 * k + 2] = src[s];
+    records[4 * k + 3] = 0;
+  }
+}
+
+/*
+ * O17: gather the pages the records name: dense page records[4k] receives
+ * page records[4k+2] of table entry records[4k+1]; descriptor rules as O10.
+ * Returns 1 if a descriptor was out of range.
+ */
+int gpbo_gather_records(const uint8_t *const *table, const int64_t *table_pages,
+                        int32_t n_src, const int32_t *records, int32_t n,
+                        int32_t page_size, int32_t row_bytes, uint8_t *dense) {
+  int bad = 0;
+  const int64_t page_bytes = (int64_t)page_size * row_bytes;
+  for (int32_t k = 0; k < n; k++) {
+    int32_t s = records[4 * k + 0], e = records[4 * k + 1], p = records[4 * k + 2];
+    uint8_t *out = dense + (int64_t)s * page_bytes;
+    if (e < 0 || p < 0) { memset(out, 0, (size_t)page_bytes); continue; }
+    if (e >= n_src || p >= table_pages[e]) {
+      bad = 1;
+      memset(out, 0, (size_t)page_bytes);
+      continue;
+    }
+    memcpy(out, table[e] + (int64_t)p * page_bytes, (size_t)page_bytes);
+  }
+  return bad;
+}
+
+/*
+ * O18: what each writer scatters (page d63fbd4, commit "counting barrier +
+ * CUDA-IPC gather": a current page has exactly one writer under the
+ * page-aligned split, and the writers are fixed per batch; page 0d87bc5,
+ * commit "prefetch staging exchange": each rank fills its own current rows
+ * into its own staging).  Writer w owns the current pages i with writer
+ * i mod W; its tokens, in token order, form list w, and list w is stored
+ * after lists 0..w-1:
+ *   writer_offsets[w]   first entry of list w; writer_offsets[W] = T  [W+1]
+ *   writer_tokens[k]    batch token of entry k                         [T]
+ *   writer_rows[k]      that token's staging row inside slab w (the
+ *                       batch staging row less w * CAP * PS)           [T]
+ *   writer_page_row0[i] entry of current page i's first token, counted
+ *                       from the start of its writer's list           [NCP]
+ * A writer holding its tokens' rows in list order scatters row k of its
+ * list to writer_rows[k] of its own slab.
+ */
+void gpbo_writer_lists(int32_t bs, int32_t page_size, int32_t n_writers,
+                       int32_t staging_cap_pages, const int32_t *prefix_pages,
+                       const int32_t *cur_tokens, const int32_t *staging_rows,
+                       int32_t *writer_offsets, int32_t *writer_tokens,
+                       int32_t *writer_rows, int32_t *writer_page_row0) {
+  const int32_t PS = page_size, W = n_writers;
+  const int64_t slab_rows = (int64_t)staging_cap_pages * PS;
+  (void)prefix_pages;
+  int32_t k = 0;
+  for (int32_t w = 0; w < W; w++) {
+    writer_offsets[w] = k;
+    int32_t i = 0, token = 0;
+    for (int32_t r = 0; r < bs; r++) {
+      int32_t C = (int32_t)ceil_div(cur_tokens[r], PS);
+      for (int32_t q = 0; q < C; q++, i++) {
+        if (i % W != w) continue;
+        writer_page_row0[i] = k - writer_offsets[w];
+        int32_t end = (q + 1) * PS < cur_tokens[r] ? (q + 1) * PS : cur_tokens[r];
+        for (int32_t j = q * PS; j < end; j++) {
+          int32_t t = token + j;
+          writer_tokens[k] = t;
+          writer_rows[k] = (int32_t)(staging_rows[t] - w * slab_rows);
+          k++;
+        }
+      }
+      token += cur_tokens[r];
+    }
+  }
+  writer_offsets[W] = k;
 }

@@ -328,6 +328,72 @@ def pin_prefetch_split(orc, batch, pl, pool, cur, dense, staging):
     assert np.all(pk == KIND_CUR) and np.array_equal(pi, np.arange(len(locs)))
 
 
+def pin_page_records(orc, batch, pl, pool, dense, staging):
+    """The gather records of the two split halves: their slots are the prefix
+    and current slot lists, each record names the page the one-shot gather
+    puts in that slot, and gathering the prefix records then the current
+    records (O17) rebuilds the one-shot dense buffer, the first pass leaving
+    every current slot untouched."""
+    PS, RB = batch.page_size, batch.row_bytes
+    pre = pl["prefix_desc"].reshape(-1, 4)
+    cur = pl["current_desc"].reshape(-1, 4)
+    assert np.array_equal(pre[:, 0], pl["prefix_slots"])
+    assert np.array_equal(cur[:, 0], pl["current_slots"])
+    assert not pre[:, 3].any() and not cur[:, 3].any()
+    kind, idx = decode(dense)
+    table = oracle.pointer_table(pool, staging.reshape(-1), batch.n_pool_entries,
+                                 batch.n_writers, batch.staging_cap_pages, PS, RB)
+    # each record's (owner, src) addresses exactly the rows its slot holds
+    for s, e, p, _ in np.concatenate([pre, cur]):
+        arena = table[e].reshape(-1, RB)
+        assert np.array_equal(arena[p * PS:(p + 1) * PS], dense[s * PS:(s + 1) * PS])
+    split = np.full_like(dense, 0xEE)
+    assert not orc.gather_records(table, pre.reshape(-1), PS, RB, split)
+    for s in cur[:, 0]:
+        assert np.all(split[s * PS:(s + 1) * PS] == 0xEE), "prefix records touched a current slot"
+    assert not orc.gather_records(table, cur.reshape(-1), PS, RB, split)
+    assert np.array_equal(split, dense), "record gather != one-shot gather"
+
+
+def pin_writer_lists(batch, pl, cur, staging):
+    """Per-writer scatter lists (page d63fbd4, commit "counting barrier +
+    CUDA-IPC gather": one writer per current page; page 0d87bc5, commit
+    "prefetch staging exchange": each rank fills its own rows into its own
+    staging).  Every token sits in exactly one list, in token order, in the
+    list of its page's writer; one torch index_copy_ per writer of its own
+    rows into its own slab rebuilds exactly the staging the single scatter
+    wrote; a page's first entry holds the page's first token."""
+    PS, RB = batch.page_size, batch.row_bytes
+    W, CAP = batch.n_writers, batch.staging_cap_pages
+    T = batch.n_cur_tokens
+    off = pl["writer_offsets"].astype(np.int64)
+    toks = pl["writer_tokens"].astype(np.int64)
+    rows = pl["writer_rows"].astype(np.int64)
+    assert len(off) == W + 1 and off[0] == 0 and off[-1] == T
+    assert np.all(np.diff(off) >= 0)
+    assert np.array_equal(np.sort(toks), np.arange(T)), "a token is missing or repeated"
+    slab_rows = CAP * PS
+    cur_t = torch.from_numpy(np.ascontiguousarray(cur))
+    rebuilt = []
+    for w in range(W):
+        seg = slice(off[w], off[w + 1])
+        tw, rw = toks[seg], rows[seg]
+        assert np.all(np.diff(tw) > 0), "list %d is not in token order" % w
+        assert np.all((rw >= PS) & (rw < slab_rows)), "a row outside slab %d" % w
+        assert np.array_equal(rw + w * slab_rows, pl["staging_rows"][tw])
+        slab = torch.zeros((slab_rows, RB), dtype=torch.uint8)
+        slab.index_copy_(0, torch.from_numpy(rw), cur_t[torch.from_numpy(tw)])
+        rebuilt.append(slab.numpy())
+    if W:
+        assert np.array_equal(np.concatenate(rebuilt), staging), \
+            "per-writer scatters != the single scatter"
+    # page i's tokens are entries writer_page_row0[i] ... of its writer's list
+    for i, (t0, n) in enumerate(zip(pl["cur_page_token0"], pl["cur_page_ntok"])):
+        w = pl["writer"][i]
+        k = off[w] + pl["writer_page_row0"][i]
+        assert np.array_equal(toks[k:k + n], np.arange(t0, t0 + n))
+
+
 def check_batch(orc, batch):
     """All per-batch pins on one batch."""
     pool, cur = tagged_values(batch)
@@ -337,6 +403,8 @@ def check_batch(orc, batch):
     pin_plan_geometry(batch, pl, dense, staging)
     pin_library_routines(batch, pl, pool, cur, dense, staging)
     pin_prefetch_split(orc, batch, pl, pool, cur, dense, staging)
+    pin_page_records(orc, batch, pl, pool, dense, staging)
+    pin_writer_lists(batch, pl, cur, staging)
 
 
 def pin_tiny_worked(orc):

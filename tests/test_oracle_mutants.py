@@ -93,6 +93,21 @@ MUTANTS = {
                            "if (p < 1 || p > n_pool_pages || seen[p])"),
     "slot_pages_reversed": ("slot_pages[s] = req_pages[s];",
                             "slot_pages[s] = req_pages[S - 1 - s];"),
+    "record_owner_of_list_index": ("records[4 * k + 1] = owner[s];",
+                                   "records[4 * k + 1] = owner[k];"),
+    "record_src_of_list_index": ("records[4 * k + 2] = src[s];",
+                                 "records[4 * k + 2] = src[k];"),
+    "record_gather_slot_field": (
+        "int32_t s = records[4 * k + 0], e = records[4 * k + 1], p = records[4 * k + 2];",
+        "int32_t s = k, e = records[4 * k + 1], p = records[4 * k + 2];"),
+    "writer_rows_global": ("writer_rows[k] = (int32_t)(staging_rows[t] - w * slab_rows);",
+                           "writer_rows[k] = (int32_t)staging_rows[t];"),
+    "writer_page_row0_global": ("writer_page_row0[i] = k - writer_offsets[w];",
+                                "writer_page_row0[i] = k;"),
+    "writer_list_skips_tail": (
+        "int32_t end = (q + 1) * PS < cur_tokens[r] ? (q + 1) * PS : cur_tokens[r];",
+        "int32_t end = (q + 1) * PS < cur_tokens[r] ? (q + 1) * PS : cur_tokens[r] - 1;"),
+    "writer_list_page_index": ("if (i % W != w) continue;", "if (q % W != w) continue;"),
 }
 
 CHILD = r"""
