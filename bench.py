@@ -44,6 +44,9 @@ def _args():
                     help="write profiles/ summaries from three rocprofv3 csv output "
                          "directories (kernel trace + stats, FETCH_SIZE, WRITE_SIZE) "
                          "and exit; runs on the host only")
+    ap.add_argument("--summarize-trace", metavar="TRACE",
+                    help="write profiles/compose_<workload>_kernels.txt from a rocprofv3 "
+                         "kernel-trace directory alone (no counter passes) and exit")
     ap.add_argument("--summarize-extras", metavar="TRACE",
                     help="write profiles/compose_<workload>_extras_kernels.txt from the "
                          "rocprofv3 kernel-trace directory of a default run and exit")
@@ -279,6 +282,8 @@ EXTRAS_TRACE_COMMAND = (
     "-d $OUT/prof_extras -o extras -- python3 $REPO/bench.py "
     "--steps 2 --warmup 1 --cpu-seconds 0")
 
+ONE_LAYER_WORKLOADS = ("medium", "multi_source", "tiny")
+
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv "
              "-d $OUT/prof_trace -o trace -- python3 $REPO/bench.py "
@@ -302,6 +307,9 @@ def _profile_commands(trace_dir, workload="traced"):
     cmds = {}
     for k, v in PROFILE_COMMANDS.items():
         v = v.replace("$OUT", "$REPO/" + out if k != "summary" else out)
+        if k == "trace" and workload in ONE_LAYER_WORKLOADS:
+            # one layer per step: more steps, so every kernel has enough calls
+            v = v.replace("--steps 3 ", "--steps 50 ")
         cmds[k] = (v + flag) if k == "summary" else v.replace("bench.py", "bench.py" + flag, 1)
     return cmds
 
@@ -332,15 +340,9 @@ def summarize_extras(trace_dir, workload="traced"):
     print("\n".join(lines))
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
-    """profiles/<kernel>_<workload>_kernels.txt (rocprofv3 kernel statistics)
-    and profiles/compose_gather_<workload>_counters.{json,txt} (HBM bytes per
-    gather launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
-    counter reads for a plain 1 GiB copy)."""
+def _kernel_table(trace_dir, workload, title):
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
-    prof = os.path.join(ROOT, "profiles")
-    os.makedirs(prof, exist_ok=True)
-    lines = ["# rocprofv3 kernel statistics, %s workload (bench.py)" % workload,
+    lines = ["# rocprofv3 kernel statistics, %s workload (%s)" % (workload, title),
              "# command: " + _profile_commands(trace_dir, workload)["trace"],
              "# source digest of %s: %s" % (", ".join(DIGEST_FILES), _source_digest()),
              "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
@@ -349,6 +351,26 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
         lines.append("%-34s %7s %12.0f %12.0f %12.0f %8.2f" % (
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]), float(r["MinNs"]),
             float(r["MaxNs"]), float(r["Percentage"])))
+    return lines
+
+
+def summarize_trace(trace_dir, workload="traced"):
+    """profiles/compose_<workload>_kernels.txt from a kernel trace alone."""
+    lines = _kernel_table(trace_dir, workload, "bench.py, kernel trace only")
+    path = os.path.join(ROOT, "profiles", "compose_%s_kernels.txt" % workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
+    """profiles/<kernel>_<workload>_kernels.txt (rocprofv3 kernel statistics)
+    and profiles/compose_gather_<workload>_counters.{json,txt} (HBM bytes per
+    gather launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
+    counter reads for a plain 1 GiB copy)."""
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    lines = _kernel_table(trace_dir, workload, "bench.py")
     with open(os.path.join(prof, "compose_%s_kernels.txt" % workload), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -393,6 +415,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     return rec
 
 
+LEAD_LAUNCHES = 64
+
+
+def _lead(runner, L, stream):
+    """GPU work to queue ahead of a timed region: gathers of the batch's
+    layers, at least LEAD_LAUNCHES of them whatever the layer count, so that
+    even on a one-layer batch the GPU is still busy with the lead while the
+    host enqueues the region's calls (a ctypes call plus launch costs the host
+    several microseconds, as long as a small layer's kernels)."""
+    n = max(L, LEAD_LAUNCHES)
+    return lambda: [runner.gather(l % L, stream) for l in range(n)]
+
+
 def _timed(stream, fn, reps, lead=None):
     """Average ms of ``fn`` over ``reps`` back-to-back calls, HIP events on
     the launch stream around the whole region.  ``lead`` enqueues GPU work
@@ -416,6 +451,9 @@ def main():
     a = _args()
     if a.summarize_profiles:
         summarize_profiles(*a.summarize_profiles, workload=a.workload)
+        return
+    if a.summarize_trace:
+        summarize_trace(a.summarize_trace, workload=a.workload)
         return
     if a.summarize_extras:
         summarize_extras(a.summarize_extras, workload=a.workload)
@@ -463,7 +501,7 @@ def main():
     # per-kernel averages: each kernel alone, launched back to back with the
     # layer loop's arguments, K*L launches per region
     reps = a.steps
-    lead = lambda: [runner.gather(l, stream) for l in range(L)]  # noqa: E731
+    lead = _lead(runner, L, stream)
     g_ms = _timed(stream, lambda: [runner.gather(l, stream) for l in range(L)], reps,
                   lead=lead) / L
     s_ms = _timed(stream, lambda: [runner.scatter(l, stream) for l in range(L)], reps,
@@ -521,7 +559,7 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
     import torch
     import gather_plan_build_amd as gpb
     import workloads
-    lead = lambda: [runner.gather(l, stream) for l in range(L)]  # noqa: E731
+    lead = _lead(runner, L, stream)
     pre_ms = _timed(stream, lambda: [runner.gather_prefix(l, stream) for l in range(L)],
                     reps, lead=lead) / L
     cur_ms = _timed(stream, lambda: [runner.gather_current(l, stream) for l in range(L)],

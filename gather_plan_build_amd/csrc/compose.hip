@@ -1,13 +1,14 @@
 // compose.hip -- per-layer current-row scatter and slot-dense page gather
 // (gfx950).
 //
-// Page d63fbd4, commit "current rows written straight into staging": per
-// layer, one index_copy_ of the current token rows into the zeroed staging
-// span, then ONE gather that fills every dense slot with a whole page from a
-// [pool entries || staging entries] pointer table (prefix slots read the
-// pool, current slots read staging slot i + 1 of their writer).  Page
-// d63fbd4, commit "compose_v2": -1 descriptors zero-fill.  Page 0d87bc5,
-// commit "fp8 index_copy_ -> uint8 views": rows are opaque bytes.
+// Page d63fbd4, commit "current rows written straight into staging": each
+// layer first copies the current token rows into staging that was zeroed
+// beforehand (index_copy_ semantics), then a single gather gives every dense
+// slot a whole page, taken from a pointer table that lists the pool arenas
+// and then the staging slabs (a prefix slot reads its pool page, a current
+// slot reads staging slot i + 1 of its writer's slab).  Page d63fbd4, commit
+// "compose_v2": an owner or src of -1 yields a zero page.  Page 0d87bc5,
+// commit "fp8 index_copy_ -> uint8 views": rows are raw bytes.
 //
 // Both per-layer kernels are HBM-bound copies with no arithmetic to speak of,
 // so the design is about the memory system only:

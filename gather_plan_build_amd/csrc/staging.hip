@@ -1,10 +1,10 @@
 // staging.hip -- the per-batch staging clear (gfx950).
 //
 // Page d63fbd4, commit "current rows written straight into staging": the
-// current rows land in a zeroed staging span, so the rows a partial last
-// current page does not fill read back as zero in the gather.  The rows the
-// scatter writes are the same in every layer of a batch, so one clear per
-// batch serves all its layers.
+// current rows are copied into staging that holds zeros, so a last current
+// page's rows beyond its request's tokens reach the dense buffer as zeros.
+// A batch's scatter writes the same staging rows in every layer, so clearing
+// once per batch is enough for all of its layers.
 //
 // A pure store stream: 256-lane workgroups, one 16-byte store per lane, 4 KiB
 // per workgroup.  Stores alone are bound by the workgroup launch rate when a

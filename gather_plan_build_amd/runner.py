@@ -2,15 +2,16 @@
 
 Once per batch: build the plan and clear both staging halves.  Per layer l:
 scatter the layer's current rows into staging half l mod 2, then gather every
-dense slot into dense half l mod 2 through the [pool entries || staging slabs]
-table of that layer (page d63fbd4, commit "current rows written straight into
-staging": one index_copy_ into the zeroed staging span, then ONE slot-dense
-gather; the parity halves keep a layer's buffers from being overwritten by the
-next one, page d63fbd4, commit "touched-pages-proportional staging").
+dense slot into dense half l mod 2 through that layer's table of pool entries
+followed by staging slabs (page d63fbd4, commit "current rows written
+straight into staging": the fill is one index_copy_ into cleared staging and
+one gather then fills the whole dense buffer; page d63fbd4, commit
+"touched-pages-proportional staging": two parity halves, so a layer never
+overwrites buffers the previous layer's consumer may still read).
 
 On one GPU every pool entry of the table is the layer's own pool arena and
 every staging entry is a slab carved from the local staging region; stream
-order replaces the cross-GPU barrier.
+order stands in for the cross-GPU barrier.
 """
 import numpy as np
 import torch

@@ -9,29 +9,54 @@
  * the slot-dense KV buffer one page per slot from a pointer table of source
  * arenas [pool entries || staging slabs].
  *
- * Source of the method (commit pages of the sglang fork, by page and commit):
- *   page d63fbd4, commit "current rows written straight into staging":
- *     fill destinations come only from a page inverse, so a per-batch
- *     staging-remapped inverse retargets the fill; the per-layer fill is one
- *     index_copy_ into the zeroed staging span; ONE slot-dense gather over a
- *     concatenated [pool || staging] pointer table, current slots carrying
- *     owner = (number of pool entries) + writer and src = staging slot;
- *     mixed_locs and staging row indices are built once per batch.
- *   page d63fbd4, commit "touched-pages-proportional staging": staging holds
- *     one round of current pages in merged-span order at slot = the page's
- *     batch current index; overflow fails fast.
- *   page d63fbd4, commit "compose_v2": descriptors of -1 zero-fill a slot.
- *   page d63fbd4, commit "cut per-layer CPU on the prefill launch path":
- *     the ragged int32 descriptors kv_lens/q_starts/q_lens/k_bases/q_bases/
- *     current_bases and the slot spans, built once per batch from batch
- *     metadata without device synchronisation.
- *   page 0d87bc5, commit "prefetch staging exchange": page id 0 is the dummy
- *     page; the staging slot of current page i is i + 1 (row block 0 unused).
- *   page 0d87bc5, commit "canonical prefix/current slot spans": the spans are
- *     the sole description of the prefix/current regions; an empty span is
- *     valid, a missing one is an error.
- *   page 0d87bc5, commit "fp8 index_copy_ -> uint8 views": rows are moved as
- *     opaque bytes, whatever their element type.
+ * Where the method comes from (commit pages of the sglang fork, cited by the
+ * page's commit hash and the commit's subject):
+ *   page d63fbd4, commit "current rows written straight into staging": the
+ *     fill kernels find their destinations through a page inverse, so one
+ *     extra inverse built per batch points them at staging instead of the
+ *     pool; each layer's fill is then a single index_copy_ of the current
+ *     rows into staging that was zeroed beforehand; a single gather then
+ *     fills every dense slot from a table that lists the pool arenas first
+ *     and the staging slabs after them (a current slot's owner is the number
+ *     of pool entries plus its writer, its src is its staging slot).
+ *     mixed_locs and the staging row of every current token do not change
+ *     from layer to layer, so they are computed once per batch.
+ *   page d63fbd4, commit "touched-pages-proportional staging": staging is
+ *     sized for the current pages of one batch only; current page i of the
+ *     batch (requests in batch order, pages in sequence order) owns the same
+ *     staging slot on every rank; running out of staging is an error.
+ *   page d63fbd4, commit "compose_v2": an owner or src of -1 means a page of
+ *     zeros.
+ *   page d63fbd4, commit "cut per-layer CPU on the prefill launch path": the
+ *     slot spans and the int32 ragged descriptors (kv_lens, q_starts, q_lens,
+ *     k_bases, q_bases, current_bases) come from the batch metadata once per
+ *     batch, with no wait on the device.
+ *   page 0d87bc5, commit "prefetch staging exchange": pool page 0 is a dummy;
+ *     staging slot 0 is left unused, so current page i sits in slot i + 1.
+ *   page 0d87bc5, commit "canonical prefix/current slot spans": the spans
+ *     alone describe where each request's prefix and current pages sit; an
+ *     empty span is fine, a missing one is an error.
+ *   page 0d87bc5, commit "fp8 index_copy_ -> uint8 views": a row is moved as
+ *     raw bytes, whatever element type it holds.
+ *
+ * How this ABI differs from the plainest signature of the three calls
+ * (plan_build; a scatter taking staging, rows, current rows and a count; a
+ * gather taking a device array of source pointers and its length):
+ *   - gpb_compose_gather takes its pointer table as a host struct
+ *     (gpb_sources, at most GPB_MAX_SOURCES = 64 entries) that the library
+ *     copies into the kernel arguments, not a device array of pointers: a
+ *     workgroup then reads its slot's arena base and page count from the
+ *     argument segment with scalar loads, and no device table has to be
+ *     built or kept coherent with the arenas.  The table also carries each
+ *     arena's size in pages, so a descriptor outside its arena is caught;
+ *   - gpb_current_row_scatter takes the staging region's size in rows
+ *     (n_staging_rows), so a row index outside it is skipped, not written;
+ *   - every per-layer call takes an optional device status word (d_status)
+ *     that kernels OR GPB_STATUS_* bits into, since a kernel cannot return
+ *     an error code;
+ *   - gpb_batch carries device copies of the three metadata arrays beside
+ *     the host copies: the host validates its copy, the kernels read theirs,
+ *     and nothing is copied or synchronised inside the call.
  *
  * Conventions for every call:
  *   - Returns GPB_OK (0) or a negative gpb_status.  Arguments are checked on

@@ -500,13 +500,14 @@ def test_index_key_twin_shares_the_plan(orc):
     """The indexer-key twin (page 0d87bc5, commit "prefetch staging exchange":
     the index fill is pointed at the same staging page inverse) composes a
     second row format with the token plan of the traced batch: 144-byte rows,
-    byte-exact against the oracle on four layers."""
+    byte-exact against the oracle on four layers, each with its own pool and
+    current-row arena and with both formats' dense halves poisoned first."""
     gpb = _gpb()
     b = workloads.make_batch("traced")
     rb = workloads.INDEX_ROW_BYTES
-    pools, curs = workloads.make_values(b, device="cuda", rotations=2)
+    pools, curs = workloads.make_values(b, device="cuda", rotations=4)
     tok = _runner(b, pools, curs)
-    ipools, icurs = workloads.make_values(b, device="cuda", rotations=2, row_bytes=rb,
+    ipools, icurs = workloads.make_values(b, device="cuda", rotations=4, row_bytes=rb,
                                           value_kind="bytes", seed=1)
     twin = gpb.ComposeRunner(gpb.BatchMeta(b.bs, b.page_size, rb, b.n_pool_pages,
                                            b.n_pool_entries, b.n_writers,
@@ -521,11 +522,17 @@ def test_index_key_twin_shares_the_plan(orc):
     want = oracle.plan_for(bi, orc)
     ipools_np = [_host(p) for p in ipools]
     icurs_np = [_host(c) for c in icurs]
+    pools_np, curs_np = [_host(p) for p in pools], [_host(c) for c in curs]
     for layer in range(4):
+        # a page either format fails to write shows against the sentinel,
+        # not against what layer - 2 left in the same half
+        tok.dense[layer % 2].fill_(POISON)
+        twin.dense[layer % 2].fill_(POISON)
         tok.layer(layer)
         twin.layer(layer)
         torch.cuda.synchronize()
         _check_layer(bi, twin, layer, want, ipools_np, icurs_np, orc)
+        _check_layer(b, tok, layer, want, pools_np, curs_np, orc, check_staging=False)
         _say("  twin layer", layer, "ok")
     assert _status(twin) == 0 and _status(tok) == 0
 
@@ -609,13 +616,14 @@ def test_grouped_formats_match_single_format(orc, seed):
 
 def test_token_and_index_twin_in_one_launch_each(orc):
     """The traced batch's token KV (1152-byte rows) and index keys (144-byte
-    rows) composed with grouped launches, four layers, byte-exact."""
+    rows) composed with grouped launches, four layers with distinct arenas and
+    poisoned dense halves, byte-exact."""
     gpb = _gpb()
     b = workloads.make_batch("traced")
     rb = workloads.INDEX_ROW_BYTES
-    pools, curs = workloads.make_values(b, device="cuda", rotations=2)
+    pools, curs = workloads.make_values(b, device="cuda", rotations=4)
     tok = _runner(b, pools, curs)
-    ipools, icurs = workloads.make_values(b, device="cuda", rotations=2, row_bytes=rb,
+    ipools, icurs = workloads.make_values(b, device="cuda", rotations=4, row_bytes=rb,
                                           value_kind="bytes", seed=1)
     bi = workloads.Batch(b.name, b.bs, b.page_size, rb, b.n_pool_pages, b.n_pool_entries,
                          b.n_writers, b.staging_cap_pages, b.prefix_pages, b.cur_tokens,
@@ -627,6 +635,8 @@ def test_token_and_index_twin_in_one_launch_each(orc):
     pools_np, curs_np = [_host(p) for p in pools], [_host(c) for c in curs]
     ipools_np, icurs_np = [_host(p) for p in ipools], [_host(c) for c in icurs]
     for layer in range(4):
+        tok.dense[layer % 2].fill_(POISON)
+        twin.dense[layer % 2].fill_(POISON)
         gpb.layer_groups([tok, twin], layer)
         torch.cuda.synchronize()
         _check_layer(b, tok, layer, want, pools_np, curs_np, orc)
