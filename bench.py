@@ -79,9 +79,9 @@ def _source_digest():
 
 
 def _traffic(workload):
-    """HBM bytes per gather launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "compose_gather_%s_counters.json" % workload)
+    """Memory bytes per one-launch-layer launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "compose_layer_%s_counters.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -267,9 +267,9 @@ def _short(name):
     kept (they tell the gather from the slot-list gather, the scatter from the
     fused fill)."""
     import re
-    for key in ("k_compose_gather", "k_row_scatter", "k_gather_groups", "k_scatter_groups",
-                "k_fill_zero", "k_plan_scan_fill", "k_plan_slots", "k_plan_tokens",
-                "copyBuffer"):
+    for key in ("k_compose_layer", "k_compose_gather", "k_row_scatter", "k_gather_groups",
+                "k_scatter_groups", "k_fill_zero", "k_plan_scan_fill", "k_plan_slots",
+                "k_plan_tokens", "copyBuffer"):
         if key in name:
             m = re.search(key + r"(<[^>]*>)?", name)
             return m.group(0).replace(" ", "")
@@ -364,10 +364,11 @@ def summarize_trace(trace_dir, workload="traced"):
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
-    """profiles/<kernel>_<workload>_kernels.txt (rocprofv3 kernel statistics)
-    and profiles/compose_gather_<workload>_counters.{json,txt} (HBM bytes per
-    gather launch from FETCH_SIZE / WRITE_SIZE, each scaled by what the same
-    counter reads for a plain 1 GiB copy)."""
+    """profiles/compose_<workload>_kernels.txt (rocprofv3 kernel statistics)
+    and profiles/compose_layer_<workload>_counters.json (bytes per launch of
+    every library kernel from FETCH_SIZE / WRITE_SIZE, each scaled by what
+    the same counter reads for a plain 1 GiB copy; the one-launch layer's
+    figure is the roofline's traffic)."""
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     lines = _kernel_table(trace_dir, workload, "bench.py")
@@ -395,7 +396,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
                            "write_kib": w_copy, "fetch_scale": f_scale,
                            "write_scale": w_scale},
            "kernels": {}}
-    for k in ("k_compose_gather<64,1,false>", "k_row_scatter<64,1,false,true>"):
+    for k in sorted(set(fetch) & set(write)):
+        if not k.startswith("k_"):
+            continue
         if k in fetch and k in write:
             fk = sum(fetch[k]) / len(fetch[k])
             wk = sum(write[k]) / len(write[k])
@@ -405,27 +408,38 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
                 "read_bytes": round(1024 * fk * f_scale),
                 "write_bytes": round(1024 * wk * w_scale),
                 "hbm_bytes_per_launch": round(1024 * (fk * f_scale + wk * w_scale))}
-    g = "k_compose_gather<64,1,false>"
-    if g in rec["kernels"]:
-        rec["hbm_bytes_per_launch"] = rec["kernels"][g]["hbm_bytes_per_launch"]
-    with open(os.path.join(prof, "compose_gather_%s_counters.json" % workload), "w") as f:
+    layer = [k for k in rec["kernels"] if k.startswith("k_compose_layer")]
+    if layer:
+        rec["kernel"] = layer[0]
+        rec["hbm_bytes_per_launch"] = rec["kernels"][layer[0]]["hbm_bytes_per_launch"]
+    with open(os.path.join(prof, "compose_layer_%s_counters.json" % workload), "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(rec, indent=1, sort_keys=True))
     return rec
 
 
-LEAD_LAUNCHES = 64
+class Lead:
+    """GPU work queued ahead of a timed region: copies of a 256 MiB buffer,
+    enough of them that the host has enqueued every call of the region
+    before the GPU reaches the region's start event (HOST_US_PER_CALL per
+    call, a generous bound on one ctypes call and its launches, plus a
+    margin).  The region then holds GPU time only, even for calls whose host
+    side is slower than their kernels (every call of a one-layer batch)."""
+    HOST_US_PER_CALL = 30.0
 
+    def __init__(self, stream):
+        import torch
+        n = 256 << 20
+        self.src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        self.dst = torch.empty_like(self.src)
+        self.copy_ms = _timed(stream, lambda: self.dst.copy_(self.src), 8)
 
-def _lead(runner, L, stream):
-    """GPU work to queue ahead of a timed region: gathers of the batch's
-    layers, at least LEAD_LAUNCHES of them whatever the layer count, so that
-    even on a one-layer batch the GPU is still busy with the lead while the
-    host enqueues the region's calls (a ctypes call plus launch costs the host
-    several microseconds, as long as a small layer's kernels)."""
-    n = max(L, LEAD_LAUNCHES)
-    return lambda: [runner.gather(l % L, stream) for l in range(n)]
+    def __call__(self, n_calls):
+        import math
+        want_ms = n_calls * self.HOST_US_PER_CALL * 1e-3 + 0.5
+        k = max(2, math.ceil(want_ms / self.copy_ms))
+        return lambda: [self.dst.copy_(self.src) for _ in range(k)]
 
 
 def _timed(stream, fn, reps, lead=None):
@@ -498,46 +512,55 @@ def main():
                       "global_batch": batch.bs, "seq_len": None,
                       "parallelism": "single GPU",
                       "algorithmic_bytes_per_layer": layer_bytes}}
-    # per-kernel averages: each kernel alone, launched back to back with the
-    # layer loop's arguments, K*L launches per region
+    # GPU-only regions, each behind a lead (see Lead): K*L back-to-back
+    # layers, and each kernel alone with the layer loop's arguments
     reps = a.steps
-    lead = _lead(runner, L, stream)
-    g_ms = _timed(stream, lambda: [runner.gather(l, stream) for l in range(L)], reps,
-                  lead=lead) / L
-    s_ms = _timed(stream, lambda: [runner.scatter(l, stream) for l in range(L)], reps,
-                  lead=lead) / L
-    # plan build + clear: host validation and four launches take longer on the
-    # host than their kernels on the GPU, so a lead of gathers keeps the GPU
-    # busy while the calls are queued
-    p_ms = _timed(stream, lambda: runner.begin_batch(stream), reps, lead=lead)
-    # host time of one gpb_plan_build call (validation + three launches, no
-    # synchronisation), for comparison with host-side plan builders
+    lead = Lead(stream)
+
+    def region(fn, calls_per_rep):
+        return _timed(stream, fn, reps, lead=lead(reps * calls_per_rep))
+
+    layer_ms = region(lambda: [runner.layer(l, stream) for l in range(L)], L) / L
+    two_ms = region(lambda: [runner.layer_two_launch(l, stream) for l in range(L)],
+                    2 * L) / L
+    g_ms = region(lambda: [runner.gather(l, stream) for l in range(L)], L) / L
+    s_ms = region(lambda: [runner.scatter(l, stream) for l in range(L)], L) / L
+    # plan build with the staging clear: three launches per batch
+    p_ms = region(lambda: runner.begin_batch(stream), 1)
+    # host time of one gpb_plan_build_clear call (validation + three
+    # launches, no synchronisation), for comparison with host-side builders
     torch.cuda.synchronize()
     n_host = 50
     t0 = time.perf_counter()
     for _ in range(n_host):
-        runner.plan.build(stream)
+        runner.begin_batch(stream)
     plan_host_us = (time.perf_counter() - t0) / n_host * 1e6
     torch.cuda.synchronize()
     g_us, s_us = g_ms * 1e3, s_ms * 1e3
-    g_bytes = runner.gather_bytes()
-    achieved = g_bytes / (g_us * 1e-6) / 1e9
-    out["us_per_layer"] = round((ms_per_step - p_ms) * 1e3 / L, 2)
-    out["pct_of_peak"] = round(100.0 * layer_bytes / (out["us_per_layer"] * 1e-6) / 1e9
-                               / HBM_PEAK_GBS, 2)
-    out["kernels_us"] = {"compose_gather": round(g_us, 2),
+    # the dominant kernel is the one-launch layer (gpb_compose_layer): one
+    # launch moves the layer's algorithmic bytes
+    achieved = layer_bytes / (layer_ms * 1e-3) / 1e9
+    out["us_per_layer"] = round(layer_ms * 1e3, 2)
+    out["pct_of_peak"] = round(100.0 * achieved / HBM_PEAK_GBS, 2)
+    out["kernels_us"] = {"compose_layer": round(layer_ms * 1e3, 2),
+                         "compose_gather": round(g_us, 2),
                          "current_row_scatter": round(s_us, 2),
-                         "plan_build_and_staging_clear": round(p_ms * 1e3, 2)}
+                         "plan_build_with_staging_clear": round(p_ms * 1e3, 2)}
+    out["two_launch_layer"] = {
+        "us_per_layer": round(two_ms * 1e3, 2),
+        "pct_of_peak": round(100.0 * layer_bytes / (two_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "gather_pct_of_peak": round(100.0 * runner.gather_bytes() / (g_us * 1e-6) / 1e9
+                                    / HBM_PEAK_GBS, 2)}
     out["plan_build_host_us"] = round(plan_host_us, 1)
     out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1),
                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(achieved / HBM_PEAK_GBS, 4),
                        "traffic": _traffic(a.workload),
-                       "kernel": "compose_gather", "bytes_per_launch": g_bytes}
+                       "kernel": "compose_layer", "bytes_per_launch": layer_bytes}
     if a.no_extras:
         a.twin_index_bytes = 0
     else:
-        _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms)
+        _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead)
     assert int(runner.status.item()) == 0
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib << 20
@@ -551,42 +574,68 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
-    """Extra figures: the step replayed as one HIP graph; the layer-ahead
-    prefetch split (the prefix gather can run a layer ahead, so the per-layer
-    critical path is the fill or scatter plus the gather of the current pages
-    only); the fused fill; the index-key twin on the same plan."""
+def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
+    """Extra figures: the step replayed as one HIP graph; the layer in one
+    launch; the layer-ahead prefetch split (the prefix gather can run a layer
+    ahead, so the per-layer critical path is the consume: the fill or
+    scatter plus the gather of the current pages), its halves alone and the
+    whole batch run with the prefetch on a second stream; the fused fill; the
+    scatter split over the writers; the index-key twin on the same plan."""
     import torch
     import gather_plan_build_amd as gpb
     import workloads
-    lead = _lead(runner, L, stream)
-    pre_ms = _timed(stream, lambda: [runner.gather_prefix(l, stream) for l in range(L)],
-                    reps, lead=lead) / L
-    cur_ms = _timed(stream, lambda: [runner.gather_current(l, stream) for l in range(L)],
-                    reps, lead=lead) / L
-    fill_ms = _timed(stream, lambda: [runner.fill(l, stream) for l in range(L)], reps,
-                     lead=lead) / L
+
+    def region(fn, calls_per_rep):
+        return _timed(stream, fn, reps, lead=lead(reps * calls_per_rep))
+
+    pre_ms = region(lambda: [runner.gather_prefix(l, stream) for l in range(L)], L) / L
+    cur_ms = region(lambda: [runner.gather_current(l, stream) for l in range(L)], L) / L
+    cons_ms = region(lambda: [runner.consume_fused(l, stream) for l in range(L)], L) / L
+    fill_ms = region(lambda: [runner.fill(l, stream) for l in range(L)], L) / L
+    own = runner.writer_rows_of(0)
+    W = len(runner.writer_counts)
+    wsc_ms = region(lambda: [runner.scatter_writers(l, own, stream) for l in range(L)],
+                    W * L) / L
+    del own
+    # the whole batch with the layer-ahead prefetch on a second stream
+    side = torch.cuda.Stream()
+    pipe = {}
+    for consume in ("fused", "scatter"):
+        ms = region(lambda: runner.run_pipelined(L, stream, side, consume=consume),
+                    4 * L + 2)
+        pipe[consume] = ms
+    # the same schedule on one stream, one launch per layer
+    ahead_ms = region(lambda: runner.run_layer_ahead(L, stream), L + 2)
+    serial_ms = region(lambda: runner.run(L, stream), L + 1)
     # the whole step captured once as a HIP graph and replayed: same kernels,
     # no per-launch host work
-    side = torch.cuda.Stream()
     side.wait_stream(stream)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
         runner.run(L, side)
     torch.cuda.synchronize()
     graph.replay()
-    graph_ms = _timed(stream, graph.replay, reps, lead=lead)
+    graph_ms = region(graph.replay, 1)
     out["graph_replay"] = {"ms_per_step": round(graph_ms, 4),
                            "us_per_layer_incl_plan": round(graph_ms * 1e3 / L, 2)}
     del graph
     out["prefetch_split"] = {
         "prefix_gather_us": round(pre_ms * 1e3, 2),
         "current_gather_us": round(cur_ms * 1e3, 2),
+        "split_over_one_shot": round((pre_ms + cur_ms) / g_ms, 4),
         "fused_fill_us": round(fill_ms * 1e3, 2),
         "consume_us": round((s_ms + cur_ms) * 1e3, 2),
+        "consume_fused_us": round(cons_ms * 1e3, 2),
         "consume_with_fused_fill_us": round((fill_ms + cur_ms) * 1e3, 2),
         "fused_fill_bytes": 3 * batch.n_cur_tokens * batch.row_bytes
-                            + 8 * batch.n_cur_tokens}
+                            + 8 * batch.n_cur_tokens,
+        "pipelined_ms_per_step": round(pipe["fused"], 4),
+        "pipelined_us_per_layer_incl_plan": round(pipe["fused"] * 1e3 / L, 2),
+        "pipelined_scatter_consume_ms_per_step": round(pipe["scatter"], 4),
+        "layer_ahead_one_launch_ms_per_step": round(ahead_ms, 4),
+        "serial_one_launch_ms_per_step": round(serial_ms, 4)}
+    out["writer_scatters"] = {"writers": W, "us_per_layer": round(wsc_ms * 1e3, 2),
+                              "single_scatter_us": round(s_ms * 1e3, 2)}
     if a.twin_index_bytes:
         rb = a.twin_index_bytes
         ipools, icurs = workloads.make_values(batch, device="cuda", row_bytes=rb,
@@ -597,17 +646,21 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms):
                           batch.prefix_pages, batch.cur_tokens, batch.req_pages),
             ipools, icurs, plan=runner.plan)
         twin.begin_batch(stream)
-        t_ms = _timed(stream, lambda: [twin.layer(l, stream) for l in range(L)], reps,
-                      lead=lead) / L
+        t_ms = region(lambda: [twin.layer(l, stream) for l in range(L)], L) / L
+        t2_ms = region(lambda: [twin.layer_two_launch(l, stream) for l in range(L)],
+                       2 * L) / L
         tb = twin.algorithmic_bytes_per_layer()
-        sep_ms = _timed(stream, lambda: [(runner.layer(l, stream), twin.layer(l, stream))
-                                         for l in range(L)], reps, lead=lead) / L
-        both_ms = _timed(stream, lambda: [gpb.layer_groups([runner, twin], l, stream)
-                                          for l in range(L)], reps, lead=lead) / L
+        sep_ms = region(lambda: [(runner.layer(l, stream), twin.layer(l, stream))
+                                 for l in range(L)], 2 * L) / L
+        both_ms = region(lambda: [gpb.layer_groups([runner, twin], l, stream)
+                                  for l in range(L)], 2 * L) / L
         both_b = runner.algorithmic_bytes_per_layer() + tb
         out["index_twin"] = {"row_bytes": rb, "us_per_layer": round(t_ms * 1e3, 2),
                              "algorithmic_bytes_per_layer": tb,
                              "gbs": round(tb / (t_ms * 1e-3) / 1e9, 1),
+                             "pct_of_peak": round(100.0 * tb / (t_ms * 1e-3) / 1e9
+                                                  / HBM_PEAK_GBS, 2),
+                             "two_launch_us_per_layer": round(t2_ms * 1e3, 2),
                              "token_and_twin_separate_us": round(sep_ms * 1e3, 2),
                              "token_and_twin_grouped_us": round(both_ms * 1e3, 2),
                              "grouped_gbs": round(both_b / (both_ms * 1e-3) / 1e9, 1)}

@@ -4,7 +4,9 @@ row scatter and slot-dense page gather (libgpb.so, HIP for gfx950).
 Importing this package loads libgpb.so and fails loudly if it is missing.
 """
 from .binding import (BatchMeta, GpbError, Plan, Sources, compose_gather,  # noqa: F401
-                      compose_gather_slots, current_row_fill,
+                      compose_gather_slots, compose_gather_records, compose_layer,
+                      compose_consume, compose_layer_ahead,
+                      current_row_fill, writer_counts,
                       compose_gather_groups, current_row_scatter_groups,
                       current_row_scatter, plan_build, plan_sizes, staging_clear,
                       strerror, LIB_PATH, PLAN_FIELDS, STATUS_BAD_DESCRIPTOR,

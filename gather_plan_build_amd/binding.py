@@ -40,7 +40,8 @@ PLAN_FIELDS = ("slot_base", "prefix_span", "current_span", "q_lens", "kv_lens",
                "owner", "src", "page_inverse", "staging_page_inverse", "writer",
                "staging_rows", "mixed_locs", "token_req", "topk_offsets", "segments",
                "prefix_slots", "current_slots", "pool_locs", "cur_page_token0",
-               "cur_page_ntok")
+               "cur_page_ntok", "prefix_desc", "current_desc", "writer_offsets",
+               "writer_tokens", "writer_rows", "writer_page_row0")
 
 
 class gpb_plan(ctypes.Structure):
@@ -99,6 +100,16 @@ def _load(path):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.gpb_plan_sizes.argtypes = [ctypes.POINTER(gpb_batch), _I32P, _I32P, _I32P]
     lib.gpb_plan_build.argtypes = [ctypes.POINTER(gpb_batch), ctypes.POINTER(gpb_plan), vp]
+    lib.gpb_plan_build_clear.argtypes = [ctypes.POINTER(gpb_batch), ctypes.POINTER(gpb_plan),
+                                         vp, i64, vp]
+    lib.gpb_writer_counts.argtypes = [ctypes.POINTER(gpb_batch), _I32P]
+    lib.gpb_compose_gather_records.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, i32, i32,
+                                               i32, i32, vp, vp]
+    lib.gpb_compose_layer.argtypes = [vp, ctypes.POINTER(gpb_sources),
+                                      ctypes.POINTER(gpb_plan), i32, i32, vp, i64, vp, i32,
+                                      i32, i32, vp, vp]
+    lib.gpb_compose_consume.argtypes = lib.gpb_compose_layer.argtypes
+    lib.gpb_compose_layer_ahead.argtypes = [vp] + list(lib.gpb_compose_layer.argtypes)
     lib.gpb_staging_clear.argtypes = [vp, i64, vp]
     lib.gpb_current_row_scatter.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp]
     lib.gpb_compose_gather.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, vp, i32,
@@ -112,20 +123,20 @@ def _load(path):
                                               i32, i32, vp, vp]
     lib.gpb_strerror.argtypes = [ctypes.c_int]
     lib.gpb_strerror.restype = ctypes.c_char_p
-    for f in ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
-              "gpb_current_row_scatter", "gpb_compose_gather",
-              "gpb_compose_gather_slots", "gpb_current_row_fill",
-              "gpb_current_row_scatter_groups", "gpb_compose_gather_groups"):
-        getattr(lib, f).restype = ctypes.c_int
+    for f in EXPORTS:
+        if f != "gpb_strerror":
+            getattr(lib, f).restype = ctypes.c_int
     return lib
 
 
-lib = _load(LIB_PATH)
-
-EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_staging_clear",
-           "gpb_current_row_scatter", "gpb_compose_gather", "gpb_compose_gather_slots",
+EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_plan_build_clear",
+           "gpb_writer_counts", "gpb_staging_clear", "gpb_current_row_scatter",
+           "gpb_compose_gather", "gpb_compose_gather_slots", "gpb_compose_gather_records",
+           "gpb_compose_layer", "gpb_compose_consume", "gpb_compose_layer_ahead",
            "gpb_current_row_fill", "gpb_current_row_scatter_groups",
            "gpb_compose_gather_groups", "gpb_strerror")
+
+lib = _load(LIB_PATH)
 
 
 class GpbError(RuntimeError):
@@ -205,6 +216,32 @@ class BatchMeta:
                    b.n_writers, b.staging_cap_pages, b.prefix_pages, b.cur_tokens,
                    b.req_pages)
 
+    def plan_key(self):
+        """What a plan depends on (page 0d87bc5, commit "descriptor cache on
+        the slot-remap objects": descriptors are cached for one batch and
+        never reused across a different page layout, slot spans, table
+        layout, device or capacity; page d63fbd4, commit "counting barrier +
+        CUDA-IPC gather": the plan cache lives on the batch's slot remap): the
+        geometry except the row size, and the three metadata arrays.  Two
+        batches with equal keys have identical plans; the device is checked
+        beside the key."""
+        import hashlib
+        c = self.c
+        h = hashlib.sha256()
+        for a in (self.h_prefix, self.h_cur, self.h_req):
+            h.update(np.int64(a.size).tobytes())
+            h.update(a.tobytes())
+        return (c.bs, c.page_size, c.n_pool_pages, c.n_pool_entries, c.n_writers,
+                c.staging_cap_pages, h.hexdigest())
+
+
+def writer_counts(meta):
+    """Entries of every writer's scatter list (host only, no device read)."""
+    out = np.zeros(max(meta.c.n_writers, 1), np.int32)
+    _check(lib.gpb_writer_counts(ctypes.byref(meta.c), out.ctypes.data_as(_I32P)),
+           "gpb_writer_counts")
+    return out[:meta.c.n_writers]
+
 
 def plan_sizes(meta):
     """(S, T, NCP) after host validation; raises GpbError on a bad batch."""
@@ -227,6 +264,10 @@ class Plan:
         self.S, self.T, self.NCP = plan_sizes(meta)
         b = meta.c
         dev = _gpu_device(device)
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        self.key = meta.plan_key()
         self.d_prefix = torch.from_numpy(meta.h_prefix).to(dev)
         self.d_cur = torch.from_numpy(meta.h_cur).to(dev)
         self.d_req = torch.from_numpy(meta.h_req).to(dev)
@@ -243,16 +284,26 @@ class Plan:
                  "topk_offsets": self.T, "segments": 4 * bs,
                  "prefix_slots": self.S - self.NCP, "current_slots": self.NCP,
                  "pool_locs": self.T, "cur_page_token0": self.NCP,
-                 "cur_page_ntok": self.NCP}
+                 "cur_page_ntok": self.NCP, "prefix_desc": 4 * (self.S - self.NCP),
+                 "current_desc": 4 * self.NCP, "writer_offsets": b.n_writers + 1,
+                 "writer_tokens": self.T, "writer_rows": self.T,
+                 "writer_page_row0": self.NCP}
         self.t = {k: torch.empty(sizes[k], dtype=torch.int32, device=dev)
                   for k in PLAN_FIELDS}
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.c = gpb_plan(*[(self.t[k].data_ptr() if sizes[k] else None)
                             for k in PLAN_FIELDS], self.status.data_ptr())
 
-    def build(self, stream=None):
-        _check(lib.gpb_plan_build(ctypes.byref(self.meta.c), ctypes.byref(self.c),
-                                  _stream(stream)), "gpb_plan_build")
+    def build(self, stream=None, clear=None):
+        """Launch the plan kernels; with ``clear`` (a uint8 device tensor) the
+        same launches also zero it (gpb_plan_build_clear)."""
+        if clear is None:
+            _check(lib.gpb_plan_build(ctypes.byref(self.meta.c), ctypes.byref(self.c),
+                                      _stream(stream)), "gpb_plan_build")
+        else:
+            _check(lib.gpb_plan_build_clear(ctypes.byref(self.meta.c), ctypes.byref(self.c),
+                                            _ptr(clear), clear.numel() * clear.element_size(),
+                                            _stream(stream)), "gpb_plan_build_clear")
         return self
 
 
@@ -312,6 +363,58 @@ def compose_gather_slots(dense, sources, slots, n_list, owner, src, n_slots, pag
                                         int(page_rows), int(row_bytes), _ptr(status),
                                         _stream(stream)),
            "gpb_compose_gather_slots")
+
+
+def compose_gather_records(dense, sources, records, n_records, n_slots, page_rows,
+                           row_bytes, status=None, stream=None):
+    """Gather the pages named by (slot, owner, src, 0) records."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_gather_records(_ptr(dense), ctypes.byref(sources.c),
+                                          _ptr(records), int(n_records), int(n_slots),
+                                          int(page_rows), int(row_bytes), _ptr(status),
+                                          _stream(stream)),
+           "gpb_compose_gather_records")
+
+
+def compose_layer(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging_rows,
+                  cur_rows, n_rows, page_rows, row_bytes, status=None, stream=None):
+    """Scatter and gather of one layer in one launch (``plan`` a Plan)."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_layer(_ptr(dense), ctypes.byref(sources.c), ctypes.byref(plan.c),
+                                 int(n_slots), int(n_cur_pages), _ptr(staging),
+                                 int(n_staging_rows), _ptr(cur_rows), int(n_rows),
+                                 int(page_rows), int(row_bytes), _ptr(status),
+                                 _stream(stream)),
+           "gpb_compose_layer")
+
+
+def compose_consume(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging_rows,
+                    cur_rows, n_rows, page_rows, row_bytes, status=None, stream=None):
+    """The consume half in one launch: scatter and current-page gather."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_consume(_ptr(dense), ctypes.byref(sources.c), ctypes.byref(plan.c),
+                                   int(n_slots), int(n_cur_pages), _ptr(staging),
+                                   int(n_staging_rows), _ptr(cur_rows), int(n_rows),
+                                   int(page_rows), int(row_bytes), _ptr(status),
+                                   _stream(stream)),
+           "gpb_compose_consume")
+
+
+def compose_layer_ahead(dense, dense_next, sources, plan, n_slots, n_cur_pages, staging,
+                        n_staging_rows, cur_rows, n_rows, page_rows, row_bytes, status=None,
+                        stream=None):
+    """This layer's consume and the next layer's prefix pages in one launch."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_layer_ahead(_ptr(dense), _ptr(dense_next), ctypes.byref(sources.c),
+                                       ctypes.byref(plan.c), int(n_slots), int(n_cur_pages),
+                                       _ptr(staging), int(n_staging_rows), _ptr(cur_rows),
+                                       int(n_rows), int(page_rows), int(row_bytes),
+                                       _ptr(status), _stream(stream)),
+           "gpb_compose_layer_ahead")
 
 
 def current_row_fill(staging, n_staging_rows, staging_rows, pool, n_pool_rows, pool_locs,

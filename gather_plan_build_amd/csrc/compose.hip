@@ -56,29 +56,42 @@ struct SrcTable {
   int32_t n;
 };
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// How a gather workgroup finds its page: dense slot k (owner[k], src[k]),
+// the k-th entry of a slot list (slots[k], then owner/src of that slot), or
+// the k-th (slot, owner, src, 0) record, one 16-byte scalar load.
+enum GatherMode { kAllSlots = 0, kSlotList = 1, kRecords = 2 };
+
 // One workgroup per unit of a slot's page, units of a page consecutive.  The
 // slot's descriptor is uniform across the workgroup: owner/src are scalar
 // loads and both buffer resources live in scalar registers.  Lane l moves
 // chunks l, l + B, ... of the unit.  An invalid or -1 descriptor gets a
-// source range of 0 bytes: every load returns zeros.  With LIST, the k-th
-// group of units serves dense slot slots[k] instead of slot k.
-template <int B, int CPT, bool LIST>
+// source range of 0 bytes: every load returns zeros.
+template <int B, int CPT, int MODE>
 __global__ __launch_bounds__(B) void k_compose_gather(
-    uint8_t *__restrict__ dense, SrcTable tbl, const int32_t *__restrict__ slots,
+    uint8_t *__restrict__ dense, SrcTable tbl, const int32_t *__restrict__ list,
     int32_t n_slots, const int32_t *__restrict__ owner, const int32_t *__restrict__ src,
     int32_t page_bytes, int32_t parts, int32_t *status) {
   const int k_unit = blockIdx.x / parts;
   const int part = blockIdx.x - k_unit * parts;
-  int slot = k_unit;
-  if (LIST) {
-    slot = slots[k_unit];
-    if (slot < 0 || slot >= n_slots) {
-      if (status && part == 0 && threadIdx.x == 0) atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
-      return;
-    }
+  int slot = k_unit, e, p;
+  if (MODE == kRecords) {
+    const i32x4 rec = reinterpret_cast<const i32x4 *>(list)[k_unit];
+    slot = rec.x;
+    e = rec.y;
+    p = rec.z;
+  } else if (MODE == kSlotList) {
+    slot = list[k_unit];
   }
-  const int e = owner[slot];
-  const int p = src[slot];
+  if (MODE != kAllSlots && (slot < 0 || slot >= n_slots)) {
+    if (status && part == 0 && threadIdx.x == 0) atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+    return;
+  }
+  if (MODE != kRecords) {
+    e = owner[slot];
+    p = src[slot];
+  }
   const bool sentinel = (e < 0) || (p < 0);
   const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
   const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
@@ -91,6 +104,92 @@ __global__ __launch_bounds__(B) void k_compose_gather(
   for (int k = 0; k < CPT; ++k) v[k] = ld16(rs, first + k * (B * 16));
 #pragma unroll
   for (int k = 0; k < CPT; ++k) st16_dense(v[k], rd, first + k * (B * 16));
+  if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
+    atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+}
+
+// One launch for a whole layer: the current-row scatter and the gather of
+// every dense slot.  The units are 1 KiB of a page, one wave each: first the
+// current pages' units (record k of the current records, tokens
+// tok0[k] .. tok0[k] + ntok[k] - 1 on it), then the prefix pages' units.  A
+// current unit first copies the current-row chunks that fall in its KiB of
+// the page into staging (the scatter: token t to staging row rows[t]), then
+// reads its KiB back from staging through its gather record and stores it
+// into the dense page, as the gather does.  Through a valid plan the chunk a
+// lane reads back is the chunk that lane wrote, so the lane's own program
+// order orders the read after the write; rows past the page's tokens read
+// the zeros the per-batch clear left.  `staging` is deliberately not
+// __restrict__: the table's staging entries alias it, and the read-back must
+// stay behind the write.  The staging stores and the read-back carry the
+// plain cache policy, so the read-back is served by the L2 the wave just
+// wrote to (the two-launch path's scatter writes through instead, since its
+// reader is another kernel); on the traced workload this makes the one
+// launch 6 us per layer faster than the scatter and gather launched apart.
+//
+// Prefix pages go to dense_pre, current pages to dense: the same buffer for
+// one layer, or the next layer's dense buffer for the prefix pages when the
+// launch is layer l's consume together with layer l + 1's prefetch (the
+// table then lists layer l + 1's pool entries and layer l's staging slabs).
+//
+// With SROWS (rows of at least 21 chunks) a unit spans at most kScalarRows
+// rows, whose staging rows are fetched once with scalar loads.
+template <int B, bool SROWS>
+__global__ __launch_bounds__(B) void k_compose_layer(
+    uint8_t *dense, uint8_t *dense_pre, SrcTable tbl, const int32_t *__restrict__ pre_desc,
+    const int32_t *__restrict__ cur_desc, const int32_t *__restrict__ tok0,
+    const int32_t *__restrict__ ntok, int32_t n_cur_units, uint8_t *staging,
+    int32_t staging_bytes, int32_t n_staging_rows, const int32_t *__restrict__ rows,
+    const uint8_t *__restrict__ cur, int32_t n_rows, int32_t row_chunks, int32_t n_slots,
+    int32_t page_bytes, int32_t parts, int32_t *status) {
+  const bool is_cur = static_cast<int>(blockIdx.x) < n_cur_units;
+  const int u = is_cur ? blockIdx.x : blockIdx.x - n_cur_units;
+  const int k = u / parts;
+  const int part = u - k * parts;
+  const i32x4 rec = reinterpret_cast<const i32x4 *>(is_cur ? cur_desc : pre_desc)[k];
+  const int slot = rec.x, e = rec.y, p = rec.z;
+  if (slot < 0 || slot >= n_slots) {
+    if (status && part == 0 && threadIdx.x == 0) atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+    return;
+  }
+  const int c = part * B + threadIdx.x;  // 16-byte chunk of the page
+  const uint32_t off = static_cast<uint32_t>(c) * 16u;
+  if (is_cur) {
+    const int t0 = tok0[k], nt = ntok[k];
+    const int j = c / row_chunks;  // row of the page
+    const int oc = c - j * row_chunks;
+    const int t = t0 + j;
+    const bool live = j < nt && off < static_cast<uint32_t>(page_bytes);
+    const bool in_rows = live && t >= 0 && t < n_rows;
+    int d;
+    if (SROWS) {
+      const int j0 = part * B / row_chunks;  // first row of the unit (uniform)
+      int srow[kScalarRows];
+#pragma unroll
+      for (int q = 0; q < kScalarRows; ++q)
+        srow[q] = rows[min(max(t0 + j0 + q, 0), n_rows - 1)];
+      d = srow[kScalarRows - 1];
+#pragma unroll
+      for (int q = kScalarRows - 2; q >= 0; --q) d = j - j0 == q ? srow[q] : d;
+    } else {
+      d = rows[in_rows ? t : 0];
+    }
+    const bool ok = in_rows && d >= 0 && d < n_staging_rows;
+    const __amdgpu_buffer_rsrc_t rc = rsrc(cur, n_rows * row_chunks * 16);
+    const __amdgpu_buffer_rsrc_t rst = rsrc(staging, staging_bytes);
+    const u32x4 v = ld16(rc, in_rows ? static_cast<uint32_t>(t * row_chunks + oc) * 16u
+                                     : kDropOffset);
+    st16_staged(v, rst, ok ? static_cast<uint32_t>(d * row_chunks + oc) * 16u : kDropOffset);
+    if (live && !ok && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
+  }
+  const bool sentinel = (e < 0) || (p < 0);
+  const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
+  const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rd =
+      rsrc((is_cur ? dense : dense_pre) + static_cast<int64_t>(slot) * page_bytes, page_bytes);
+  // a current page's bytes were just written by this very wave: read them
+  // back through the cache; pool pages are streamed
+  st16_dense(is_cur ? ld16_staged(rs, off) : ld16(rs, off), rd, off);
   if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
     atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
 }
@@ -277,8 +376,8 @@ extern "C" int gpb_compose_gather(void *d_dense, const gpb_sources *table,
   const int64_t parts = ceil_div64(page_bytes / 16, static_cast<int64_t>(B) * CPT);
   const int64_t grid = parts * n_slots;
   if (grid > INT32_MAX) return GPB_ERANGE;
-  return launch(k_compose_gather<B, CPT, false>, dim3(static_cast<uint32_t>(grid)), dim3(B),
-                as_stream(stream), d_dense, t, nullptr, n_slots, d_owner, d_src,
+  return launch(k_compose_gather<B, CPT, kAllSlots>, dim3(static_cast<uint32_t>(grid)),
+                dim3(B), as_stream(stream), d_dense, t, nullptr, n_slots, d_owner, d_src,
                 page_bytes, parts, d_status);
 }
 
@@ -303,9 +402,120 @@ extern "C" int gpb_compose_gather_slots(void *d_dense, const gpb_sources *table,
   const int64_t parts = ceil_div64(page_bytes / 16, static_cast<int64_t>(B) * CPT);
   const int64_t grid = parts * n_list;
   if (grid > INT32_MAX) return GPB_ERANGE;
-  return launch(k_compose_gather<B, CPT, true>, dim3(static_cast<uint32_t>(grid)), dim3(B),
-                as_stream(stream), d_dense, t, d_slots, n_slots, d_owner, d_src,
+  return launch(k_compose_gather<B, CPT, kSlotList>, dim3(static_cast<uint32_t>(grid)),
+                dim3(B), as_stream(stream), d_dense, t, d_slots, n_slots, d_owner, d_src,
                 page_bytes, parts, d_status);
+}
+
+extern "C" int gpb_compose_gather_records(void *d_dense, const gpb_sources *table,
+                                          const int32_t *d_records, int32_t n_records,
+                                          int32_t n_slots, int32_t page_rows,
+                                          int32_t row_bytes, int32_t *d_status,
+                                          void *stream) {
+  using namespace gpb;
+  constexpr int B = GPB_GATHER_BLOCK, CPT = GPB_GATHER_CPT;
+  SrcTable t;
+  int64_t page_bytes = 0;
+  int rc = check_gather(table, n_slots, page_rows, row_bytes, d_status, &t, &page_bytes);
+  if (rc != GPB_OK) return rc;
+  if (n_records < 0) return GPB_EINVAL;
+  if (n_records == 0) return GPB_OK;
+  if (!d_dense || !d_records || n_slots == 0) return GPB_EINVAL;
+  if (!aligned(d_dense, 16) || !aligned(d_records, 16)) return GPB_EALIGN;
+  const int64_t parts = ceil_div64(page_bytes / 16, static_cast<int64_t>(B) * CPT);
+  const int64_t grid = parts * n_records;
+  if (grid > INT32_MAX) return GPB_ERANGE;
+  return launch(k_compose_gather<B, CPT, kRecords>, dim3(static_cast<uint32_t>(grid)),
+                dim3(B), as_stream(stream), d_dense, t, d_records, n_slots, nullptr, nullptr,
+                page_bytes, parts, d_status);
+}
+
+namespace gpb {
+namespace {
+// The layer in one launch (with_prefix; prefix pages into d_dense_pre) or
+// its consume half only: the same kernel over all units, or over the current
+// pages' units alone.
+int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
+                  const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
+                  void *d_staging, int64_t n_staging_rows, const void *d_cur_rows,
+                  int32_t n_rows, int32_t page_rows, int32_t row_bytes, int32_t *d_status,
+                  void *stream, bool with_prefix) {
+  constexpr int B = 64;
+  SrcTable t;
+  int64_t page_bytes = 0;
+  int rc = check_gather(table, n_slots, page_rows, row_bytes, d_status, &t, &page_bytes);
+  if (rc != GPB_OK) return rc;
+  if (!plan || n_cur_pages < 0 || n_cur_pages > n_slots || n_rows < 0 || n_staging_rows < 0)
+    return GPB_EINVAL;
+  // every current page holds at least one current row
+  if (n_cur_pages > n_rows) return GPB_EINVAL;
+  if (n_staging_rows > INT32_MAX) return GPB_ERANGE;
+  if (n_slots == 0) return GPB_OK;
+  const int32_t n_prefix = n_slots - n_cur_pages;
+  if (!d_dense || (with_prefix && n_prefix > 0 && (!plan->d_prefix_desc || !d_dense_pre)))
+    return GPB_EINVAL;
+  if (with_prefix && !aligned(d_dense_pre, 16)) return GPB_EALIGN;
+  if (n_cur_pages > 0 && (!plan->d_current_desc || !plan->d_cur_page_token0 ||
+                          !plan->d_cur_page_ntok || !d_staging ||
+                          (n_rows > 0 && (!plan->d_staging_rows || !d_cur_rows))))
+    return GPB_EINVAL;
+  if (!aligned(d_dense, 16) || !aligned(plan->d_prefix_desc, 16) ||
+      !aligned(plan->d_current_desc, 16) || !aligned(plan->d_cur_page_token0, 4) ||
+      !aligned(plan->d_cur_page_ntok, 4) || !aligned(plan->d_staging_rows, 4) ||
+      !aligned(d_staging, 16) || !aligned(d_cur_rows, 16))
+    return GPB_EALIGN;
+  const int64_t row_chunks = row_bytes / 16;
+  const int64_t cur_bytes = static_cast<int64_t>(n_rows) * row_bytes;
+  const int64_t staging_bytes = n_staging_rows * row_bytes;
+  if (cur_bytes > INT32_MAX || staging_bytes > INT32_MAX) return GPB_ERANGE;
+  const int64_t parts = ceil_div64(page_bytes / 16, B);
+  const int64_t grid = parts * (with_prefix ? n_slots : n_cur_pages);
+  if (grid > INT32_MAX) return GPB_ERANGE;
+  if (grid == 0) return GPB_OK;
+  // a unit of B chunks touches at most 2 + (B - 2) / row_chunks rows
+  const bool srows = 2 + (B - 2) / row_chunks <= kScalarRows;
+  const auto kernel = srows ? k_compose_layer<B, true> : k_compose_layer<B, false>;
+  return launch(kernel, dim3(static_cast<uint32_t>(grid)), dim3(B), as_stream(stream),
+                d_dense, with_prefix ? d_dense_pre : d_dense, t, plan->d_prefix_desc,
+                plan->d_current_desc,
+                plan->d_cur_page_token0, plan->d_cur_page_ntok,
+                static_cast<int32_t>(parts * n_cur_pages), d_staging, staging_bytes,
+                n_staging_rows, plan->d_staging_rows, d_cur_rows, n_rows,
+                static_cast<int32_t>(row_chunks), n_slots, page_bytes, parts, d_status);
+}
+}  // namespace
+}  // namespace gpb
+
+extern "C" int gpb_compose_layer(void *d_dense, const gpb_sources *table,
+                                 const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
+                                 void *d_staging, int64_t n_staging_rows,
+                                 const void *d_cur_rows, int32_t n_rows, int32_t page_rows,
+                                 int32_t row_bytes, int32_t *d_status, void *stream) {
+  return gpb::compose_layer(d_dense, d_dense, table, plan, n_slots, n_cur_pages, d_staging,
+                            n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
+                            d_status, stream, true);
+}
+
+extern "C" int gpb_compose_layer_ahead(void *d_dense, void *d_dense_next,
+                                       const gpb_sources *table, const gpb_plan *plan,
+                                       int32_t n_slots, int32_t n_cur_pages, void *d_staging,
+                                       int64_t n_staging_rows, const void *d_cur_rows,
+                                       int32_t n_rows, int32_t page_rows, int32_t row_bytes,
+                                       int32_t *d_status, void *stream) {
+  return gpb::compose_layer(d_dense, d_dense_next, table, plan, n_slots, n_cur_pages,
+                            d_staging, n_staging_rows, d_cur_rows, n_rows, page_rows,
+                            row_bytes, d_status, stream, true);
+}
+
+extern "C" int gpb_compose_consume(void *d_dense, const gpb_sources *table,
+                                   const gpb_plan *plan, int32_t n_slots,
+                                   int32_t n_cur_pages, void *d_staging,
+                                   int64_t n_staging_rows, const void *d_cur_rows,
+                                   int32_t n_rows, int32_t page_rows, int32_t row_bytes,
+                                   int32_t *d_status, void *stream) {
+  return gpb::compose_layer(d_dense, nullptr, table, plan, n_slots, n_cur_pages, d_staging,
+                            n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
+                            d_status, stream, false);
 }
 
 namespace gpb {

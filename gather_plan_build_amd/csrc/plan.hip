@@ -13,19 +13,26 @@
 // previous one's outputs:
 //   1. k_plan_scan_fill: workgroup 0 runs wave-level exclusive scans over the
 //      per-request counts (slots n, tokens c, current pages C) and writes the
-//      spans and ragged descriptors; the other workgroups fill both page
-//      inverses with -1.
+//      spans and ragged descriptors, then the first entry of every writer's
+//      scatter list; the next workgroups fill both page inverses with -1 and
+//      the rest, when the caller passes a staging region, zero it (the
+//      per-batch clear rides in the same launch).
 //   2. k_plan_slots: one lane per dense slot -> slot page, page inverse,
 //      gather descriptor, writer, staging page inverse, the slot's place in
-//      the prefix or current slot list, and a current page's token range.
+//      the prefix or current slot list and its gather record, a current
+//      page's token range and its first entry in its writer's list.
 //   3. k_plan_tokens: one lane per current token -> staging row through the
 //      staging page inverse, mixed_locs, the per-token expansions (request
-//      row id, top-k offset) and the token's pool row.
+//      row id, top-k offset), the token's pool row and its entry in its
+//      writer's list.
 // Request lookups in 2 and 3 are binary searches over the scanned bases,
-// staged in LDS.
+// staged in LDS.  A current page's first entry in its writer's list sums the
+// shortfalls of earlier requests' last pages on the same writer: a loop over
+// the earlier requests, from LDS, per current page.
 #include <algorithm>
 #include <vector>
 
+#include "buffer_io.h"
 #include "gpb_common.h"
 
 namespace gpb {
@@ -43,6 +50,11 @@ struct PlanArgs {
   int32_t *token_req, *topk_offsets, *segments;
   int32_t *prefix_slots, *current_slots, *pool_locs;
   int32_t *cur_page_token0, *cur_page_ntok;
+  int32_t *prefix_desc, *current_desc;
+  int32_t *writer_offsets, *writer_tokens, *writer_rows, *writer_page_row0;
+  uint8_t *clear;        // staging region zeroed by the fill workgroups
+  int64_t clear_bytes;
+  int32_t fill_blocks;   // workgroups 1 .. fill_blocks fill the inverses
   int32_t *status;
 };
 
@@ -62,6 +74,54 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
     if (lane >= d) v += t;
   }
   return v;
+}
+
+constexpr int kWriterChunk = 1024;  // writers whose token counts fit the LDS pass
+
+// Tokens of every writer (page d63fbd4, commit "counting barrier + CUDA-IPC
+// gather": each current page has one writer; writer of batch page i is
+// i mod W) and their exclusive sums, the first entry of each writer's list.
+// Writer w holds n_w = ceil((NCP - w) / W) pages; all of them are full
+// except the last page of a request, which lacks C_r * PS - c_r tokens and
+// belongs to writer (first current page of r + C_r - 1) mod W.  The
+// shortfalls are summed per writer in LDS, a chunk of writers at a time.
+__device__ void writer_offsets(const PlanArgs &a, int ncp) {
+  __shared__ int short_by[kWriterChunk];
+  __shared__ int chunk_carry;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) chunk_carry = 0;
+  for (int w0 = 0; w0 < a.w; w0 += kWriterChunk) {
+    for (int k = tid; k < kWriterChunk; k += kBlock) short_by[k] = 0;
+    __syncthreads();
+    for (int r = tid; r < a.bs; r += kBlock) {
+      const int c = a.c[r];
+      const int C = (c + a.ps - 1) / a.ps;
+      if (C == 0 || C * a.ps == c) continue;
+      const int last = a.q_bases[r] / a.ps + C - 1;
+      const int w = last % a.w - w0;
+      if (w >= 0 && w < kWriterChunk) atomicAdd(&short_by[w], C * a.ps - c);
+    }
+    __syncthreads();
+    // exclusive sum over the chunk's writers, one wave, 64 writers a pass
+    if (tid < 64) {
+      int carry = chunk_carry;
+      const int n = min(kWriterChunk, a.w - w0);
+      for (int b = 0; b < n; b += 64) {
+        const int w = w0 + b + lane;
+        int tok = 0;
+        if (b + lane < n) {
+          const int pages = ncp > w ? (ncp - 1 - w) / a.w + 1 : 0;
+          tok = pages * a.ps - short_by[b + lane];
+        }
+        const int inc = wave_inclusive_scan(tok, lane);
+        if (b + lane < n) a.writer_offsets[w] = carry + inc - tok;
+        carry += __shfl(inc, 63, 64);
+      }
+      if (lane == 0) chunk_carry = carry;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.writer_offsets[a.w] = chunk_carry;
 }
 
 __device__ void scan_requests(const PlanArgs &a) {
@@ -124,14 +184,31 @@ __device__ void scan_requests(const PlanArgs &a) {
     carry_C = all_C;
     __syncthreads();  // wave_tot is reused by the next tile
   }
+  // q_bases written above by this workgroup are read back after the
+  // workgroup barrier that opens writer_offsets
+  writer_offsets(a, carry_C);
 }
 
+constexpr int kClearBytes = kBlock * 16;  // staging bytes per clear workgroup
+
+// Workgroup 0 scans the requests; workgroups 1 .. fill_blocks fill both page
+// inverses with -1; the workgroups after them zero the staging region, 4 KiB
+// each (the per-batch clear, page d63fbd4, commit "current rows written
+// straight into staging": the scatter writes into zeroed staging).  The
+// clear's last workgroup gets a buffer range that ends with the region.
 __global__ __launch_bounds__(kBlock) void k_plan_scan_fill(PlanArgs a) {
   if (blockIdx.x == 0) {
     scan_requests(a);
     return;
   }
-  const int stride = (gridDim.x - 1) * kBlock;
+  if (static_cast<int>(blockIdx.x) > a.fill_blocks) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x - 1 - a.fill_blocks) * kClearBytes;
+    const int64_t left = a.clear_bytes - base;
+    const int32_t range = left < kClearBytes ? static_cast<int32_t>(left) : kClearBytes;
+    st16(u32x4{0, 0, 0, 0}, rsrc(a.clear + base, range), threadIdx.x * 16u);
+    return;
+  }
+  const int stride = a.fill_blocks * kBlock;
   for (int p = (blockIdx.x - 1) * kBlock + threadIdx.x; p < a.n_pool_pages; p += stride) {
     a.page_inverse[p] = -1;
     a.staging_page_inverse[p] = -1;
@@ -150,9 +227,19 @@ __device__ __forceinline__ int find_request(const int32_t *base, int bs, int x) 
   return lo;
 }
 
+// Writer of request r's last current page and the tokens that page lacks
+// (0 when the page is full or r has no current page), from global memory.
+__device__ __forceinline__ void last_page_shortfall(const PlanArgs &a, int r, int *w,
+                                                    int *lack) {
+  const int c = a.c[r];
+  const int C = (c + a.ps - 1) / a.ps;
+  *lack = C * a.ps - c;
+  *w = C > 0 ? (a.q_bases[r] / a.ps + C - 1) % a.w : -1;
+}
+
 __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
   __shared__ int32_t s_base[kLdsRequests], s_P[kLdsRequests], s_qb[kLdsRequests],
-      s_qs[kLdsRequests], s_c[kLdsRequests];
+      s_qs[kLdsRequests], s_c[kLdsRequests], s_lw[kLdsRequests], s_lack[kLdsRequests];
   const bool lds = a.bs <= kLdsRequests;
   if (lds) {
     for (int r = threadIdx.x; r < a.bs; r += kBlock) {
@@ -161,6 +248,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
       s_qb[r] = a.q_bases[r];
       s_qs[r] = a.q_starts[r];
       s_c[r] = a.c[r];
+      last_page_shortfall(a, r, &s_lw[r], &s_lack[r]);
     }
     __syncthreads();
   }
@@ -182,12 +270,18 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
   }
   a.page_inverse[page] = s;
   const int cur_before = qb[r] / a.ps;  // current pages of earlier requests
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
   if (j < P) {  // prefix slot: modulo-owned pool entry, the page itself
-    a.owner[s] = page % a.np;
+    const int e = page % a.np;
+    a.owner[s] = e;
     a.src[s] = page;
     const int u = s - cur_before;
-    if (within(u, a.n_slots - a.n_cur_pages)) a.prefix_slots[u] = s;
-    else flag_bad_input(a);
+    if (within(u, a.n_slots - a.n_cur_pages)) {
+      a.prefix_slots[u] = s;
+      reinterpret_cast<i32x4 *>(a.prefix_desc)[u] = i32x4{s, e, page, 0};
+    } else {
+      flag_bad_input(a);
+    }
   } else {      // current page i of the batch
     const int i = cur_before + (j - P);
     const int w = i % a.w;
@@ -200,6 +294,21 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
       a.current_slots[i] = s;
       a.cur_page_token0[i] = qs[r] + k * a.ps;
       a.cur_page_ntok[i] = min(a.ps, cv[r] - k * a.ps);
+      reinterpret_cast<i32x4 *>(a.current_desc)[i] = i32x4{s, a.np + w, i + 1, 0};
+      // first entry of page i in writer w's list: the i div W earlier pages
+      // of w, all full but for the last pages of earlier requests
+      int lack = 0;
+      for (int q = 0; q < r; ++q) {
+        int lw, lk;
+        if (lds) {
+          lw = s_lw[q];
+          lk = s_lack[q];
+        } else {
+          last_page_shortfall(a, q, &lw, &lk);
+        }
+        lack += lw == w ? lk : 0;
+      }
+      a.writer_page_row0[i] = (i / a.w) * a.ps - lack;
     } else {
       flag_bad_input(a);
     }
@@ -208,7 +317,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_slots(PlanArgs a) {
 
 __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   __shared__ int32_t s_qs[kLdsRequests], s_base[kLdsRequests], s_P[kLdsRequests],
-      s_cb[kLdsRequests], s_kb[kLdsRequests];
+      s_cb[kLdsRequests], s_kb[kLdsRequests], s_qb[kLdsRequests];
   const bool lds = a.bs <= kLdsRequests;
   if (lds) {
     for (int r = threadIdx.x; r < a.bs; r += kBlock) {
@@ -217,6 +326,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
       s_P[r] = a.P[r];
       s_cb[r] = a.current_bases[r];
       s_kb[r] = a.k_bases[r];
+      s_qb[r] = a.q_bases[r];
     }
     __syncthreads();
   }
@@ -225,6 +335,7 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   const int32_t *Pv = lds ? s_P : a.P;
   const int32_t *cb = lds ? s_cb : a.current_bases;
   const int32_t *kb = lds ? s_kb : a.k_bases;
+  const int32_t *qb = lds ? s_qb : a.q_bases;
   const int t = blockIdx.x * kBlock + threadIdx.x;
   if (t >= a.n_rows) return;
   const int r = find_request(qs, a.bs, t);
@@ -237,11 +348,24 @@ __global__ __launch_bounds__(kBlock) void k_plan_tokens(PlanArgs a) {
   }
   const int loc = page * a.ps + j % a.ps;  // the token's pool row
   const int spage = a.staging_page_inverse[loc / a.ps];
-  a.staging_rows[t] = spage * a.ps + loc % a.ps;
+  const int row = spage * a.ps + loc % a.ps;
+  a.staging_rows[t] = row;
   a.mixed_locs[t] = cb[r] + j;
   a.token_req[t] = r;
   a.topk_offsets[t] = kb[r];
   a.pool_locs[t] = loc;
+  // the token's entry in its page writer's scatter list, with its row inside
+  // that writer's slab
+  const int i = qb[r] / a.ps + j / a.ps;
+  const int w = i % a.w;
+  const int e = within(i, a.n_cur_pages)
+                    ? a.writer_offsets[w] + a.writer_page_row0[i] + j % a.ps : -1;
+  if (!within(e, a.n_rows)) {
+    flag_bad_input(a);
+    return;
+  }
+  a.writer_tokens[e] = t;
+  a.writer_rows[e] = row - w * a.cap * a.ps;
 }
 
 // Host-side validation of a batch; the rules and their order match the
@@ -282,40 +406,56 @@ int validate_batch(const gpb_batch *b, int32_t *S_out, int32_t *T_out,
   return GPB_OK;
 }
 
-bool ok_array(const void *p, int64_t n) { return n == 0 || (p && aligned(p, 4)); }
-
-}  // namespace
-}  // namespace gpb
-
-extern "C" int gpb_plan_sizes(const gpb_batch *batch, int32_t *n_slots,
-                              int32_t *n_rows, int32_t *n_cur_pages) {
-  return gpb::validate_batch(batch, n_slots, n_rows, n_cur_pages);
+bool ok_array(const void *p, int64_t n, uintptr_t align = 4) {
+  return n == 0 || (p && aligned(p, align));
 }
 
-extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *stream) {
-  using namespace gpb;
+// Host-side counts of the per-writer scatter lists: writer w holds the
+// current pages i with i mod W == w, each with its request's tokens on it.
+void writer_counts(const gpb_batch *b, int32_t *counts) {
+  for (int32_t w = 0; w < b->n_writers; ++w) counts[w] = 0;
+  int64_t i = 0;
+  for (int32_t r = 0; r < b->bs; ++r) {
+    const int64_t c = b->h_cur_tokens[r];
+    for (int64_t k = 0; k * b->page_size < c; ++k, ++i)
+      counts[i % b->n_writers] +=
+          static_cast<int32_t>(std::min<int64_t>(b->page_size, c - k * b->page_size));
+  }
+}
+
+int plan_build(const gpb_batch *b, const gpb_plan *o, void *d_clear, int64_t clear_bytes,
+               void *stream) {
   int32_t S = 0, T = 0, NCP = 0;
   int rc = validate_batch(b, &S, &T, &NCP);
   if (rc != GPB_OK) return rc;
   if (!o) return GPB_EINVAL;
-  const int64_t bs = b->bs, npp = b->n_pool_pages;
-  struct Need { const void *p; int64_t n; };
+  if (clear_bytes < 0 || (clear_bytes > 0 && !d_clear)) return GPB_EINVAL;
+  if (clear_bytes % 16 != 0 || (clear_bytes > 0 && !aligned(d_clear, 16))) return GPB_EALIGN;
+  const int64_t bs = b->bs, npp = b->n_pool_pages, W = b->n_writers;
+  struct Need { const void *p; int64_t n; uintptr_t align; };
   const Need need[] = {
-      {b->d_prefix_pages, bs}, {b->d_cur_tokens, bs}, {b->d_req_pages, S},
-      {o->d_slot_base, bs}, {o->d_prefix_span, 2 * bs}, {o->d_current_span, 2 * bs},
-      {o->d_q_lens, bs}, {o->d_kv_lens, bs}, {o->d_q_starts, bs},
-      {o->d_k_bases, bs}, {o->d_q_bases, bs}, {o->d_current_bases, bs},
-      {o->d_slot_pages, S}, {o->d_owner, S}, {o->d_src, S},
-      {o->d_page_inverse, npp}, {o->d_staging_page_inverse, npp},
-      {o->d_writer, NCP}, {o->d_staging_rows, T}, {o->d_mixed_locs, T},
-      {o->d_token_req, T}, {o->d_topk_offsets, T}, {o->d_segments, 4 * bs},
-      {o->d_prefix_slots, S - NCP}, {o->d_current_slots, NCP}, {o->d_pool_locs, T},
-      {o->d_cur_page_token0, NCP}, {o->d_cur_page_ntok, NCP}};
+      {b->d_prefix_pages, bs, 4}, {b->d_cur_tokens, bs, 4}, {b->d_req_pages, S, 4},
+      {o->d_slot_base, bs, 4}, {o->d_prefix_span, 2 * bs, 4}, {o->d_current_span, 2 * bs, 4},
+      {o->d_q_lens, bs, 4}, {o->d_kv_lens, bs, 4}, {o->d_q_starts, bs, 4},
+      {o->d_k_bases, bs, 4}, {o->d_q_bases, bs, 4}, {o->d_current_bases, bs, 4},
+      {o->d_slot_pages, S, 4}, {o->d_owner, S, 4}, {o->d_src, S, 4},
+      {o->d_page_inverse, npp, 4}, {o->d_staging_page_inverse, npp, 4},
+      {o->d_writer, NCP, 4}, {o->d_staging_rows, T, 4}, {o->d_mixed_locs, T, 4},
+      {o->d_token_req, T, 4}, {o->d_topk_offsets, T, 4}, {o->d_segments, 4 * bs, 4},
+      {o->d_prefix_slots, S - NCP, 4}, {o->d_current_slots, NCP, 4},
+      {o->d_pool_locs, T, 4}, {o->d_cur_page_token0, NCP, 4},
+      {o->d_cur_page_ntok, NCP, 4}, {o->d_prefix_desc, S - NCP, 16},
+      {o->d_current_desc, NCP, 16}, {o->d_writer_offsets, W + 1, 4},
+      {o->d_writer_tokens, T, 4}, {o->d_writer_rows, T, 4},
+      {o->d_writer_page_row0, NCP, 4}};
   for (const Need &e : need) {
     if (e.n > 0 && !e.p) return GPB_EINVAL;
-    if (!ok_array(e.p, e.n)) return GPB_EALIGN;
+    if (!ok_array(e.p, e.n, e.align)) return GPB_EALIGN;
   }
   if (o->d_status && !aligned(o->d_status, 4)) return GPB_EALIGN;
+  const int64_t fill_blocks = std::min<int64_t>(256, ceil_div64(npp, kBlock * 4));
+  const int64_t clear_blocks = ceil_div64(clear_bytes, kClearBytes);
+  if (1 + fill_blocks + clear_blocks > INT32_MAX) return GPB_ERANGE;
   PlanArgs a;
   a.bs = b->bs; a.ps = b->page_size; a.np = b->n_pool_entries; a.w = b->n_writers;
   a.cap = b->staging_cap_pages; a.n_pool_pages = b->n_pool_pages;
@@ -333,15 +473,45 @@ extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *strea
   a.prefix_slots = o->d_prefix_slots; a.current_slots = o->d_current_slots;
   a.pool_locs = o->d_pool_locs;
   a.cur_page_token0 = o->d_cur_page_token0; a.cur_page_ntok = o->d_cur_page_ntok;
+  a.prefix_desc = o->d_prefix_desc; a.current_desc = o->d_current_desc;
+  a.writer_offsets = o->d_writer_offsets; a.writer_tokens = o->d_writer_tokens;
+  a.writer_rows = o->d_writer_rows; a.writer_page_row0 = o->d_writer_page_row0;
+  a.clear = static_cast<uint8_t *>(d_clear);
+  a.clear_bytes = clear_bytes;
+  a.fill_blocks = static_cast<int32_t>(fill_blocks);
   a.status = o->d_status;
 
   hipStream_t st = as_stream(stream);
-  // workgroup 0 scans; the rest fill the inverses (4 entries per lane-pass)
-  const int64_t fill_blocks = std::min<int64_t>(256, ceil_div64(npp, kBlock * 4));
-  rc = launch(k_plan_scan_fill, dim3(1 + fill_blocks), dim3(kBlock), st, a);
+  rc = launch(k_plan_scan_fill, dim3(static_cast<uint32_t>(1 + fill_blocks + clear_blocks)),
+              dim3(kBlock), st, a);
   if (rc == GPB_OK && S > 0)
     rc = launch(k_plan_slots, dim3(ceil_div64(S, kBlock)), dim3(kBlock), st, a);
   if (rc == GPB_OK && T > 0)
     rc = launch(k_plan_tokens, dim3(ceil_div64(T, kBlock)), dim3(kBlock), st, a);
   return rc;
+}
+
+}  // namespace
+}  // namespace gpb
+
+extern "C" int gpb_plan_sizes(const gpb_batch *batch, int32_t *n_slots,
+                              int32_t *n_rows, int32_t *n_cur_pages) {
+  return gpb::validate_batch(batch, n_slots, n_rows, n_cur_pages);
+}
+
+extern "C" int gpb_plan_build(const gpb_batch *b, const gpb_plan *o, void *stream) {
+  return gpb::plan_build(b, o, nullptr, 0, stream);
+}
+
+extern "C" int gpb_plan_build_clear(const gpb_batch *b, const gpb_plan *o, void *d_staging,
+                                    int64_t staging_bytes, void *stream) {
+  return gpb::plan_build(b, o, d_staging, staging_bytes, stream);
+}
+
+extern "C" int gpb_writer_counts(const gpb_batch *b, int32_t *h_counts) {
+  const int rc = gpb::validate_batch(b, nullptr, nullptr, nullptr);
+  if (rc != GPB_OK) return rc;
+  if (!h_counts) return GPB_EINVAL;
+  gpb::writer_counts(b, h_counts);
+  return GPB_OK;
 }

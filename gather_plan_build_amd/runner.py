@@ -1,19 +1,21 @@
 """The per-batch / per-layer compose loop on one GPU.
 
-Once per batch: build the plan and clear both staging halves.  Per layer l:
-scatter the layer's current rows into staging half l mod 2, then gather every
-dense slot into dense half l mod 2 through that layer's table of pool entries
-followed by staging slabs (page d63fbd4, commit "current rows written
-straight into staging": the fill is one index_copy_ into cleared staging and
-one gather then fills the whole dense buffer; page d63fbd4, commit
+Once per batch: build the plan and clear both staging halves (one call, the
+clear riding in the plan's first launch).  Per layer l: scatter the layer's
+current rows into staging half l mod 2, then gather every dense slot into
+dense half l mod 2 through that layer's table of pool entries followed by
+staging slabs (page d63fbd4, commit "current rows written straight into
+staging": the fill is one index_copy_ into cleared staging and one gather
+then fills the whole dense buffer; page d63fbd4, commit
 "touched-pages-proportional staging": two parity halves, so a layer never
-overwrites buffers the previous layer's consumer may still read).
+overwrites buffers the previous layer's consumer may still read).  By
+default the two steps share one launch (gpb_compose_layer);
+``layer_two_launch`` runs them as two.
 
 On one GPU every pool entry of the table is the layer's own pool arena and
 every staging entry is a slab carved from the local staging region; stream
 order stands in for the cross-GPU barrier.
 """
-import numpy as np
 import torch
 
 from . import binding as B
@@ -49,19 +51,20 @@ class ComposeRunner:
             plan = B.Plan(meta, device)
         else:
             # a twin row format (e.g. indexer keys next to token KV) reuses the
-            # batch's plan: no plan array depends on the row size
+            # batch's plan: no plan array depends on the row size.  Anything
+            # else a plan depends on must match (page 0d87bc5, commit
+            # "descriptor cache on the slot-remap objects": no reuse across a
+            # different layout, spans, device or capacity).
             B.plan_sizes(meta)
-            m = plan.meta.c
-            same = ((m.bs, m.page_size, m.n_pool_pages, m.n_pool_entries, m.n_writers,
-                     m.staging_cap_pages) == (b.bs, b.page_size, b.n_pool_pages,
-                                              b.n_pool_entries, b.n_writers,
-                                              b.staging_cap_pages)
-                    and np.array_equal(plan.meta.h_prefix, meta.h_prefix)
-                    and np.array_equal(plan.meta.h_cur, meta.h_cur)
-                    and np.array_equal(plan.meta.h_req, meta.h_req))
-            if not same:
+            if plan.key != meta.plan_key():
                 raise ValueError("a shared plan must come from the same batch metadata "
                                  "(only the row size may differ)")
+            dev = torch.device(device)
+            if dev.index is None:
+                dev = torch.device("cuda", torch.cuda.current_device())
+            if plan.device != dev:
+                raise ValueError("a shared plan lives on %s, the runner on %s"
+                                 % (plan.device, dev))
         self.plan = plan
         self.owns_plan = plan.meta is meta
         self.S, self.T = self.plan.S, self.plan.T
@@ -82,6 +85,7 @@ class ComposeRunner:
         self.dense = [torch.empty(max(self.S * self.ps * self.rb, 16), dtype=torch.uint8,
                                   device=dev) for _ in range(PARITY)]
         self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.writer_counts = B.writer_counts(meta)
         self.tables = {}
         for k, pool in enumerate(self.pools):
             for h in range(PARITY):
@@ -92,10 +96,12 @@ class ComposeRunner:
 
     def begin_batch(self, stream=None):
         """Plan build (unless the plan belongs to a twin) + clear of both
-        staging halves (once per batch)."""
+        staging halves (once per batch), the clear riding in the plan's first
+        launch."""
         if self.owns_plan:
-            self.plan.build(stream)
-        B.staging_clear(self.staging_all, stream=stream)
+            self.plan.build(stream, clear=self.staging_all)
+        else:
+            B.staging_clear(self.staging_all, stream=stream)
 
     def scatter(self, layer, stream=None):
         h, k = layer % PARITY, layer % len(self.curs)
@@ -110,6 +116,11 @@ class ComposeRunner:
                          stream)
 
     def layer(self, layer, stream=None):
+        """One layer: the scatter and the gather in one launch."""
+        self.layer_fused(layer, stream)
+
+    def layer_two_launch(self, layer, stream=None):
+        """One layer as the scatter launch followed by the gather launch."""
         self.scatter(layer, stream)
         self.gather(layer, stream)
 
@@ -120,17 +131,97 @@ class ComposeRunner:
 
     def gather_prefix(self, layer, stream=None):
         h, k = layer % PARITY, layer % len(self.pools)
-        t = self.plan.t
-        B.compose_gather_slots(self.dense[h], self.tables[(k, h)], t["prefix_slots"],
-                               self.S - self.plan.NCP, t["owner"], t["src"], self.S,
-                               self.ps, self.rb, self.status, stream)
+        B.compose_gather_records(self.dense[h], self.tables[(k, h)],
+                                 self.plan.t["prefix_desc"], self.S - self.plan.NCP,
+                                 self.S, self.ps, self.rb, self.status, stream)
 
     def gather_current(self, layer, stream=None):
         h, k = layer % PARITY, layer % len(self.pools)
-        t = self.plan.t
-        B.compose_gather_slots(self.dense[h], self.tables[(k, h)], t["current_slots"],
-                               self.plan.NCP, t["owner"], t["src"], self.S, self.ps,
-                               self.rb, self.status, stream)
+        B.compose_gather_records(self.dense[h], self.tables[(k, h)],
+                                 self.plan.t["current_desc"], self.plan.NCP, self.S,
+                                 self.ps, self.rb, self.status, stream)
+
+    def layer_fused(self, layer, stream=None):
+        """The layer's scatter and gather in one launch."""
+        h, k = layer % PARITY, layer % len(self.pools)
+        B.compose_layer(self.dense[h], self.tables[(k, h)], self.plan, self.S, self.plan.NCP,
+                        self.staging[h], self.staging_rows_total,
+                        self.curs[layer % len(self.curs)], self.T, self.ps, self.rb,
+                        self.status, stream)
+
+    def consume_fused(self, layer, stream=None):
+        """The consume half in one launch: the scatter and the gather of the
+        current pages."""
+        h, k = layer % PARITY, layer % len(self.pools)
+        B.compose_consume(self.dense[h], self.tables[(k, h)], self.plan, self.S,
+                          self.plan.NCP, self.staging[h], self.staging_rows_total,
+                          self.curs[layer % len(self.curs)], self.T, self.ps, self.rb,
+                          self.status, stream)
+
+    def ahead(self, layer, stream=None):
+        """Layer l's consume and layer l + 1's prefix pages in one launch
+        (the table: layer l + 1's pool entries, layer l's staging slabs)."""
+        h, hn = layer % PARITY, (layer + 1) % PARITY
+        k = (layer + 1) % len(self.pools)
+        B.compose_layer_ahead(self.dense[h], self.dense[hn], self.tables[(k, h)], self.plan,
+                              self.S, self.plan.NCP, self.staging[h],
+                              self.staging_rows_total, self.curs[layer % len(self.curs)],
+                              self.T, self.ps, self.rb, self.status, stream)
+
+    def run_layer_ahead(self, n_layers, stream=None, before_prefetch=None,
+                        after_consume=None):
+        """The batch with the layer-ahead prefetch on one stream, one launch
+        per layer: the prefix pages of layer 0, then for each layer l its
+        consume together with the prefix pages of layer l + 1
+        (gpb_compose_layer_ahead), the last layer's consume alone.  The dense
+        half layer l + 1 fills was last read by layer l - 1, whose launch
+        came before.  Hooks as in run_pipelined, both on ``stream``."""
+        self.begin_batch(stream)
+        if n_layers == 0:
+            return
+        if before_prefetch is not None:
+            before_prefetch(0, stream)
+        self.gather_prefix(0, stream)
+        for l in range(n_layers):
+            if l + 1 < n_layers:
+                if before_prefetch is not None:
+                    before_prefetch(l + 1, stream)
+                self.ahead(l, stream)
+            else:
+                self.consume_fused(l, stream)
+            if after_consume is not None:
+                after_consume(l, stream)
+
+    def writer_rows_of(self, layer):
+        """Each writer's own current rows in its list order (what a rank that
+        computed them would hold): gathered here from the layer's current
+        rows by the plan's writer_tokens.  Input preparation for
+        scatter_writers, not part of the compose."""
+        cur = self.curs[layer % len(self.curs)].view(-1, self.rb)
+        toks = self.plan.t["writer_tokens"].long()
+        out, at = [], 0
+        for n in self.writer_counts:
+            out.append(cur.index_select(0, toks[at:at + int(n)]).contiguous())
+            at += int(n)
+        return out
+
+    def scatter_writers(self, layer, writer_rows, stream=None):
+        """The scatter as W writers would run it, each on its own slab only
+        (page d63fbd4, commit "counting barrier + CUDA-IPC gather": one writer
+        per current page): writer w copies its rows ``writer_rows[w]`` (in
+        its list order) to its list's slab-local staging rows."""
+        h = layer % PARITY
+        slab_rows = self.cap * self.ps
+        slab_bytes = slab_rows * self.rb
+        base = self.staging[h]
+        rows = self.plan.t["writer_rows"]
+        at = 0
+        for w, n in enumerate(self.writer_counts):
+            n = int(n)
+            B.current_row_scatter(base[w * slab_bytes:(w + 1) * slab_bytes], slab_rows,
+                                  rows[at:at + n] if n else None, writer_rows[w], n, self.rb,
+                                  self.status, stream)
+            at += n
 
     def fill(self, layer, stream=None):
         """Fused current fill: current rows to staging and to their pool rows
@@ -156,6 +247,66 @@ class ComposeRunner:
         self.begin_batch(stream)
         for l in range(n_layers):
             self.layer(l, stream)
+
+    def run_pipelined(self, n_layers, stream, side, consume="fused",
+                      before_prefetch=None, after_consume=None):
+        """The batch with the layer-ahead prefetch (page 0d87bc5, commit
+        "prefetch staging exchange"): the prefix pages of layer l + 1 are
+        gathered on ``side`` while layer l is consumed on ``stream``; the
+        consume of layer l is its current-row fill into staging and the
+        gather of its current pages into the dense half whose prefix is
+        already there.  Events order the two streams:
+
+        - the prefix gather of layer l waits for the consume of layer l - 2,
+          the last user of the same dense half (the parity-half reuse
+          distance of page d63fbd4, commit "touched-pages-proportional
+          staging");
+        - the consume of layer l waits for the prefix gather of layer l.
+
+        ``consume``: "fused" (one launch), "scatter" (scatter, then the
+        current-page gather) or "fill" (fused fill into staging and pool,
+        then the current-page gather).  ``before_prefetch(l, side)`` runs on
+        the side stream just before layer l's prefix gather, and
+        ``after_consume(l, stream)`` on the main stream right after layer l's
+        consume, before the dense half is handed back (a stand-in for the
+        attention that reads it).  Both streams keep the default priority."""
+        import torch
+        self.begin_batch(stream)
+        planned = torch.cuda.Event()
+        planned.record(stream)
+        side.wait_event(planned)
+        free = [None] * PARITY
+        ready = [torch.cuda.Event() for _ in range(PARITY)]
+
+        def prefetch(l):
+            h = l % PARITY
+            if free[h] is not None:
+                side.wait_event(free[h])
+            if before_prefetch is not None:
+                before_prefetch(l, side)
+            self.gather_prefix(l, side)
+            ready[h].record(side)
+
+        if n_layers > 0:
+            prefetch(0)
+        for l in range(n_layers):
+            if l + 1 < n_layers:
+                prefetch(l + 1)
+            h = l % PARITY
+            stream.wait_event(ready[h])
+            if consume == "fused":
+                self.consume_fused(l, stream)
+            else:
+                if consume == "fill":
+                    self.fill(l, stream)
+                else:
+                    self.scatter(l, stream)
+                self.gather_current(l, stream)
+            if after_consume is not None:
+                after_consume(l, stream)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            free[h] = ev
 
     def dense_of(self, layer):
         """Dense half written by ``layer`` as [S*PS, RB] uint8 (valid until

@@ -177,7 +177,25 @@ typedef struct gpb_batch {
  *                         slot_pages[its slot] * page_size + j mod page_size
  *                                                                       [T]
  *   cur_page_token0[i]    first current token held by current page i   [NCP]
- *   cur_page_ntok[i]      current tokens it holds (1..page_size)       [NCP] */
+ *   cur_page_ntok[i]      current tokens it holds (1..page_size)       [NCP]
+ *   prefix_desc[4u..4u+3] gather record of prefix_slots[u]: (slot, owner,
+ *                         src, 0); 16-byte aligned           [4 * (S - NCP)]
+ *   current_desc[4i..]    gather record of current_slots[i]   [4 * NCP]
+ * Per-writer scatter lists (page d63fbd4, commit "counting barrier +
+ * CUDA-IPC gather": one writer per current page, writers fixed per batch;
+ * page 0d87bc5, commit "prefetch staging exchange": each rank fills its own
+ * current rows into its own staging).  List w holds, in token order, the
+ * tokens on the current pages of writer w; the lists are stored one after
+ * another:
+ *   writer_offsets[w]     first entry of list w; [W] = T               [W+1]
+ *   writer_tokens[k]      batch token of entry k                        [T]
+ *   writer_rows[k]        its staging row inside slab w: the batch
+ *                         staging row less w * CAP * page_size          [T]
+ *   writer_page_row0[i]   entry of current page i's first token within
+ *                         its writer's list                           [NCP]
+ * A writer holding the rows of its list's tokens, in list order, fills its
+ * own slab with gpb_current_row_scatter(slab, CAP * page_size,
+ * writer_rows + writer_offsets[w], rows, count, ...). */
 typedef struct gpb_plan {
   int32_t *d_slot_base, *d_prefix_span, *d_current_span;
   int32_t *d_q_lens, *d_kv_lens, *d_q_starts;
@@ -189,6 +207,8 @@ typedef struct gpb_plan {
   int32_t *d_token_req, *d_topk_offsets, *d_segments;
   int32_t *d_prefix_slots, *d_current_slots, *d_pool_locs;
   int32_t *d_cur_page_token0, *d_cur_page_ntok;
+  int32_t *d_prefix_desc, *d_current_desc;
+  int32_t *d_writer_offsets, *d_writer_tokens, *d_writer_rows, *d_writer_page_row0;
   int32_t *d_status;  /* optional (NULL): GPB_STATUS_* bits the kernels OR in */
 } gpb_plan;
 
@@ -212,15 +232,35 @@ int gpb_plan_sizes(const gpb_batch *batch, int32_t *n_slots, int32_t *n_rows,
                    int32_t *n_cur_pages);
 
 /* Validate on the host, then launch the plan kernels on `stream`: a scan
- * kernel (wave-level exclusive scans of the per-request counts, which also
- * fills both page inverses with -1), a per-slot kernel (slot pages, page
- * inverse, descriptors, writers, staging inverse) and a per-token kernel
- * (staging rows through the staging inverse, mixed_locs).  The plan is
- * layer-invariant: build it once per batch.  Errors: GPB_EINVAL, GPB_EPAGE,
- * GPB_ECAPACITY, GPB_ERANGE (S*page_size, T, n_pool_pages*page_size or
- * W*CAP*page_size beyond INT32_MAX), GPB_EALIGN (int32 arrays not 4-byte
- * aligned), GPB_EHIP. */
+ * kernel (wave-level exclusive scans of the per-request counts and the
+ * writer list offsets; its other workgroups fill both page inverses with
+ * -1), a per-slot kernel (slot pages, page inverse, descriptors, records,
+ * writers, staging inverse) and a per-token kernel (staging rows through the
+ * staging inverse, mixed_locs, writer lists).  The plan is layer-invariant:
+ * build it once per batch.  Errors: GPB_EINVAL, GPB_EPAGE, GPB_ECAPACITY,
+ * GPB_ERANGE (S*page_size, T, n_pool_pages*page_size or W*CAP*page_size
+ * beyond INT32_MAX), GPB_EALIGN (int32 arrays not 4-byte aligned, the two
+ * record arrays not 16-byte aligned), GPB_EHIP. */
 int gpb_plan_build(const gpb_batch *batch, const gpb_plan *plan, void *stream);
+
+/* gpb_plan_build plus the per-batch staging clear in the same three launches:
+ * the first launch's spare workgroups also zero staging_bytes bytes at
+ * d_staging (the whole staging region, both parity halves if the caller
+ * keeps two), which gpb_staging_clear would otherwise do in a launch of its
+ * own.  staging_bytes = 0 clears nothing.  Errors as gpb_plan_build, plus
+ * GPB_EINVAL (staging_bytes < 0, or d_staging NULL with staging_bytes > 0)
+ * and GPB_EALIGN (staging_bytes % 16 != 0 or d_staging not 16-byte
+ * aligned). */
+int gpb_plan_build_clear(const gpb_batch *batch, const gpb_plan *plan, void *d_staging,
+                         int64_t staging_bytes, void *stream);
+
+/* Host only: validate the batch and write, for every writer w < n_writers,
+ * the number of entries of its scatter list (tokens on the current pages
+ * i with i mod n_writers == w) to h_counts[w].  These are the sizes of the
+ * per-writer scatters; they equal the differences of the plan's
+ * writer_offsets, without reading device memory.  Errors as gpb_plan_sizes,
+ * plus GPB_EINVAL for h_counts NULL. */
+int gpb_writer_counts(const gpb_batch *batch, int32_t *h_counts);
 
 /* Zero `n_bytes` bytes at d_ptr (n_bytes a multiple of 16, d_ptr 16-byte
  * aligned): the per-batch clear of the staging region, so the rows of a last
@@ -295,6 +335,70 @@ int gpb_current_row_fill(void *d_staging, int64_t n_staging_rows,
                          int64_t n_pool_rows, const int32_t *d_pool_locs,
                          const void *d_cur_rows, int32_t n_rows, int32_t row_bytes,
                          int32_t *d_status, void *stream);
+
+/* Per layer, the layer-ahead split's halves through the plan's records: as
+ * gpb_compose_gather_slots, but record k (four int32: slot, owner, src, 0;
+ * the plan's prefix_desc or current_desc, 16-byte aligned) names both the
+ * dense slot and its page, so a workgroup reads one 16-byte record instead
+ * of a slot and then that slot's descriptor.  A record whose slot is outside
+ * [0, n_slots) is skipped and GPB_STATUS_BAD_DESCRIPTOR is ORed into
+ * *d_status.  Errors as gpb_compose_gather_slots. */
+int gpb_compose_gather_records(void *d_dense, const gpb_sources *table,
+                               const int32_t *d_records, int32_t n_records,
+                               int32_t n_slots, int32_t page_rows, int32_t row_bytes,
+                               int32_t *d_status, void *stream);
+
+/* Per layer, in one launch: the current-row scatter of gpb_current_row_scatter
+ * (rows d_cur_rows, destinations plan->d_staging_rows, into d_staging of
+ * n_staging_rows rows) and the gather of all n_slots dense slots of
+ * gpb_compose_gather, with the same result as the two calls in order.  The
+ * plan gives the records (prefix_desc, current_desc), the tokens of each
+ * current page (cur_page_token0, cur_page_ntok) and the staging rows;
+ * n_cur_pages is its NCP.  The workgroups that gather a current page first
+ * write that page's current rows into staging and then read the page back
+ * through the table, so the table's staging entries must be the slabs the
+ * staging rows address (the layout gpb_plan_build assumes: slab w at
+ * d_staging + w * CAP * page_rows * row_bytes), and the staging rows a batch
+ * does not write must hold zeros (gpb_staging_clear or gpb_plan_build_clear
+ * once per batch).  Rows must not repeat (the plan's do not).  Errors as the
+ * two calls, plus GPB_EINVAL for plan NULL or n_cur_pages outside
+ * [0, min(n_slots, n_rows)]. */
+int gpb_compose_layer(void *d_dense, const gpb_sources *table, const gpb_plan *plan,
+                      int32_t n_slots, int32_t n_cur_pages, void *d_staging,
+                      int64_t n_staging_rows, const void *d_cur_rows, int32_t n_rows,
+                      int32_t page_rows, int32_t row_bytes, int32_t *d_status,
+                      void *stream);
+
+/* Per layer, the consume half of the layer-ahead split in one launch (page
+ * 0d87bc5, commit "prefetch staging exchange": the consume step fills the
+ * current rows into staging and gathers every current page from it into
+ * the dense buffer whose prefix pages were gathered ahead): gpb_compose_layer
+ * for the current pages only; prefix slots of d_dense are not touched.
+ * Arguments, requirements and errors as gpb_compose_layer. */
+int gpb_compose_consume(void *d_dense, const gpb_sources *table, const gpb_plan *plan,
+                        int32_t n_slots, int32_t n_cur_pages, void *d_staging,
+                        int64_t n_staging_rows, const void *d_cur_rows, int32_t n_rows,
+                        int32_t page_rows, int32_t row_bytes, int32_t *d_status,
+                        void *stream);
+
+/* Per layer, the layer-ahead split in one launch per layer (page 0d87bc5,
+ * commit "prefetch staging exchange": the prefix of the next layer's dense
+ * buffer is gathered a layer ahead while this layer is consumed): this
+ * layer's consume (gpb_compose_consume into d_dense) and the next layer's
+ * prefix pages (the plan's prefix_desc records gathered into d_dense_next),
+ * in one launch.  The table lists the next layer's pool entries followed by
+ * this layer's staging slabs.  Equivalent to gpb_compose_consume(d_dense,
+ * ...) followed by gpb_compose_gather_records(d_dense_next, table,
+ * prefix_desc, ...); d_dense and d_dense_next must not overlap.  A batch of
+ * L layers runs as the prefix records of layer 0, then this call for layers
+ * 0 .. L - 2, then gpb_compose_consume for layer L - 1.  Requirements and
+ * errors as gpb_compose_layer, plus GPB_EINVAL for d_dense_next NULL (with
+ * prefix pages) and GPB_EALIGN for it misaligned. */
+int gpb_compose_layer_ahead(void *d_dense, void *d_dense_next, const gpb_sources *table,
+                            const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
+                            void *d_staging, int64_t n_staging_rows, const void *d_cur_rows,
+                            int32_t n_rows, int32_t page_rows, int32_t row_bytes,
+                            int32_t *d_status, void *stream);
 
 /* Several row formats composed on one plan in one launch each (page 0d87bc5,
  * commit "prefetch staging exchange": the indexer-key fill reuses the token

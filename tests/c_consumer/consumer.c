@@ -91,10 +91,12 @@ static int same_device_bytes(const void *a, const void *b, size_t n) {
 }
 
 /* The remaining entry points against the layer just composed by the core
- * calls: the prefetch split (prefix slots, then current slots) and the
- * grouped gather must reproduce its dense buffer; the grouped scatter and the
- * fused fill must reproduce its staging, and the fill must leave each current
- * row at its pool row and every other pool byte as it was. */
+ * calls: the prefetch split (prefix slots, then current slots, by slot list
+ * and by record) and the grouped gather must reproduce its dense buffer; the
+ * grouped scatter, the fused fill and the per-writer scatters must reproduce
+ * its staging, and the fill must leave each current row at its pool row and
+ * every other pool byte as it was; the one-launch layer and the fused
+ * consume must reproduce both; the plan build with clear zeroes staging. */
 static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_sources *t,
                               int32_t S, int32_t T, int32_t NCP, void *d_pool, void *d_cur,
                               void *d_stag, void *d_dense, const uint8_t *h_pool,
@@ -165,13 +167,115 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
     fprintf(stderr, "fused fill pool differs\n");
     return 9;
   }
+  /* the split halves through the plan's records */
+  HCHECK(hipMemset(d_dense2, 0xEE, dense_bytes + 16));
+  CHECK(gpb_compose_gather_records(d_dense2, t, p->d_prefix_desc, S - NCP, S, b->page_size,
+                                   b->row_bytes, d_status, st));
+  CHECK(gpb_compose_gather_records(d_dense2, t, p->d_current_desc, NCP, S, b->page_size,
+                                   b->row_bytes, d_status, st));
+  HCHECK(hipStreamSynchronize(st));
+  if (!same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+    fprintf(stderr, "record gathers differ from the one-shot gather\n");
+    return 10;
+  }
+
+  /* the layer in one launch, and the consume half in one launch after the
+   * prefix records, each into a cleared second staging region (the table's
+   * staging entries are that region's slabs) */
+  gpb_sources t2 = *t;
+  for (int w = 0; w < b->n_writers; w++)
+    t2.base[b->n_pool_entries + w] =
+        (uint8_t *)d_stag2 + (size_t)w * b->staging_cap_pages * PS * RB;
+  for (int pass = 0; pass < 3; pass++) {
+    CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
+    HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
+    if (pass == 0) {
+      CHECK(gpb_compose_layer(d_dense2, &t2, p, S, NCP, d_stag2, (int64_t)stag_rows, d_cur, T,
+                              b->page_size, b->row_bytes, d_status, st));
+    } else if (pass == 2) {
+      /* this layer's consume and the "next" layer's prefix pages, here into
+       * the same buffer's prefix slots through a separate pointer */
+      CHECK(gpb_compose_layer_ahead(d_dense2, d_dense2, &t2, p, S, NCP, d_stag2,
+                                    (int64_t)stag_rows, d_cur, T, b->page_size, b->row_bytes,
+                                    d_status, st));
+    } else {
+      CHECK(gpb_compose_gather_records(d_dense2, &t2, p->d_prefix_desc, S - NCP, S,
+                                       b->page_size, b->row_bytes, d_status, st));
+      CHECK(gpb_compose_consume(d_dense2, &t2, p, S, NCP, d_stag2, (int64_t)stag_rows, d_cur,
+                                T, b->page_size, b->row_bytes, d_status, st));
+    }
+    HCHECK(hipStreamSynchronize(st));
+    if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB) ||
+        !same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+      fprintf(stderr, "%s differs from the two-call layer\n",
+              pass == 0 ? "one-launch layer" : pass == 1 ? "fused consume" : "layer ahead");
+      return 11;
+    }
+  }
+
+  /* the scatter as one call per writer, each writer's own rows in its list
+   * order into its own slab, sized on the host by gpb_writer_counts */
+  {
+    const int32_t W = b->n_writers;
+    int32_t *counts = calloc((size_t)W, 4), *toks = malloc(4 * (size_t)T + 4);
+    uint8_t *own = malloc((size_t)T * RB + 16);
+    void *d_own;
+    HCHECK(hipMalloc(&d_own, (size_t)T * RB + 16));
+    CHECK(gpb_writer_counts(b, counts));
+    HCHECK(hipMemcpy(toks, p->d_writer_tokens, 4 * (size_t)T, hipMemcpyDeviceToHost));
+    for (int32_t k = 0; k < T; k++) {
+      if (toks[k] < 0 || toks[k] >= T) return 12;
+      memcpy(own + (size_t)k * RB, h_cur + (size_t)toks[k] * RB, RB);
+    }
+    if (T) HCHECK(hipMemcpy(d_own, own, (size_t)T * RB, hipMemcpyHostToDevice));
+    CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
+    const size_t slab_rows = (size_t)b->staging_cap_pages * PS;
+    size_t at = 0;
+    for (int32_t w = 0; w < W; w++) {
+      CHECK(gpb_current_row_scatter((uint8_t *)d_stag2 + (size_t)w * slab_rows * RB,
+                                    (int64_t)slab_rows, p->d_writer_rows + at,
+                                    (uint8_t *)d_own + at * RB, counts[w], b->row_bytes,
+                                    d_status, st));
+      at += (size_t)counts[w];
+    }
+    HCHECK(hipStreamSynchronize(st));
+    int ok = at == (size_t)T && same_device_bytes(d_stag2, d_stag, stag_rows * RB);
+    HCHECK(hipFree(d_own));
+    free(counts);
+    free(toks);
+    free(own);
+    if (!ok) {
+      fprintf(stderr, "per-writer scatters differ from the single scatter\n");
+      return 12;
+    }
+  }
+
+  /* the plan build with the staging clear in its first launch: the same
+   * plan, and the staging region all zeros */
+  HCHECK(hipMemset(d_stag2, 0x5A, stag_rows * RB));
+  CHECK(gpb_plan_build_clear(b, p, d_stag2, (int64_t)(stag_rows * RB), st));
+  HCHECK(hipStreamSynchronize(st));
+  {
+    uint8_t *z = calloc(stag_rows * RB + 1, 1), *h = malloc(stag_rows * RB + 1);
+    HCHECK(hipMemcpy(h, d_stag2, stag_rows * RB, hipMemcpyDeviceToHost));
+    int zero = memcmp(z, h, stag_rows * RB) == 0;
+    free(z);
+    free(h);
+    if (!zero) {
+      fprintf(stderr, "plan build with clear left staging bytes set\n");
+      return 13;
+    }
+  }
+
   int32_t status = -1;
   HCHECK(hipMemcpy(&status, d_status, 4, hipMemcpyDeviceToHost));
   if (status != 0) { fprintf(stderr, "status %d after the other entry points\n", status); return 5; }
   HCHECK(hipFree(d_dense2));
   HCHECK(hipFree(d_stag2));
   HCHECK(hipFree(d_pool2));
-  printf("c consumer: slot-list gather, grouped calls and fused fill agree\n");
+  printf("c consumer: slot-list and record gathers, grouped calls, fused fill, one-launch "
+         "layer, fused consume, layer ahead, per-writer scatters and plan build with clear "
+         "agree\n");
   return 0;
 }
 
@@ -221,8 +325,10 @@ static int run(const char *in, const char *out) {
 
   /* plan outputs in the header's order, with their sizes */
   const int64_t bs = b.bs, npp = b.n_pool_pages;
+  const int64_t W = b.n_writers;
   const int64_t sizes[] = {bs, 2 * bs, 2 * bs, bs, bs, bs, bs, bs, bs, S, S, S, npp, npp,
-                           NCP, T, T, T, T, 4 * bs, S - NCP, NCP, T, NCP, NCP};
+                           NCP, T, T, T, T, 4 * bs, S - NCP, NCP, T, NCP, NCP,
+                           4 * (S - NCP), 4 * (int64_t)NCP, W + 1, T, T, NCP};
   enum { NF = sizeof sizes / sizeof sizes[0] };
   int32_t *outs[NF];
   for (int k = 0; k < NF; k++) HCHECK(hipMalloc((void **)&outs[k], 4 * (size_t)sizes[k] + 4));
@@ -234,7 +340,9 @@ static int run(const char *in, const char *out) {
                           &p.d_staging_rows, &p.d_mixed_locs, &p.d_token_req,
                           &p.d_topk_offsets, &p.d_segments, &p.d_prefix_slots,
                           &p.d_current_slots, &p.d_pool_locs, &p.d_cur_page_token0,
-                          &p.d_cur_page_ntok};
+                          &p.d_cur_page_ntok, &p.d_prefix_desc, &p.d_current_desc,
+                          &p.d_writer_offsets, &p.d_writer_tokens, &p.d_writer_rows,
+                          &p.d_writer_page_row0};
   for (int k = 0; k < NF; k++) *fields[k] = outs[k];
   p.d_status = d_status;
 

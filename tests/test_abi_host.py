@@ -13,6 +13,7 @@ import pytest
 import gather_plan_build_amd as gpb
 from gather_plan_build_amd import binding as B
 import oracle
+import pins
 import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -157,6 +158,92 @@ def test_slot_gather_and_fill_argument_checks():
     assert f(a, 10, a, a, 100, a, a, 4, 1000, None, None) == B.EALIGN
 
 
+def test_record_gather_argument_checks():
+    g = B.lib.gpb_compose_gather_records
+    a = 0x100000
+    good = B.Sources([(a, 10)])
+    assert g(a, ctypes.byref(good.c), a, 0, 4, 64, 1152, None, None) == B.OK
+    assert g(a, ctypes.byref(good.c), a, -1, 4, 64, 1152, None, None) == B.EINVAL
+    assert g(a, ctypes.byref(good.c), None, 3, 4, 64, 1152, None, None) == B.EINVAL
+    assert g(a, ctypes.byref(good.c), a + 4, 3, 4, 64, 1152, None, None) == B.EALIGN
+    assert g(a + 4, ctypes.byref(good.c), a, 3, 4, 64, 1152, None, None) == B.EALIGN
+    assert g(a, ctypes.byref(good.c), a, 3, 0, 64, 1152, None, None) == B.EINVAL
+    assert g(a, None, a, 3, 4, 64, 1152, None, None) == B.EINVAL
+
+
+def test_one_launch_layer_argument_checks():
+    a = 0x100000
+    good = B.Sources([(a, 10), (a, 4)])
+    p = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+    ahead = B.lib.gpb_compose_layer_ahead
+    # the next layer's dense buffer is required (with prefix pages) and aligned
+    assert ahead(a, None, ctypes.byref(good.c), ctypes.byref(p), 4, 1, a, 10, a, 5, 64, 1152,
+                 None, None) == B.EINVAL
+    assert ahead(a, a + 8, ctypes.byref(good.c), ctypes.byref(p), 4, 1, a, 10, a, 5, 64,
+                 1152, None, None) == B.EALIGN
+    for f in (B.lib.gpb_compose_layer, B.lib.gpb_compose_consume,
+              lambda *x: ahead(x[0], a, *x[1:])):
+        # dense, table, plan, S, NCP, staging, staging rows, cur, T, PS, RB
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 0, 0, a, 10, a, 0, 64, 1152,
+                 None, None) == B.OK
+        assert f(a, ctypes.byref(good.c), None, 4, 1, a, 10, a, 5, 64, 1152,
+                 None, None) == B.EINVAL
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 4, 5, a, 10, a, 5, 64, 1152,
+                 None, None) == B.EINVAL                       # NCP > S
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 4, 2, a, 10, a, 1, 64, 1152,
+                 None, None) == B.EINVAL                       # NCP > T
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 4, 1, None, 10, a, 5, 64, 1152,
+                 None, None) == B.EINVAL
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 4, 1, a + 8, 10, a, 5, 64, 1152,
+                 None, None) == B.EALIGN
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 4, 1, a, 1 << 40, a, 5, 64,
+                 1152, None, None) == B.ERANGE
+        assert f(a, ctypes.byref(good.c), ctypes.byref(p), 4, 1, a, 10, a, 1 << 22, 64,
+                 1152, None, None) == B.ERANGE               # > 2 GiB of rows
+        q = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+        q.d_current_desc = a + 4
+        assert f(a, ctypes.byref(good.c), ctypes.byref(q), 4, 1, a, 10, a, 5, 64, 1152,
+                 None, None) == B.EALIGN
+        q.d_current_desc = None
+        assert f(a, ctypes.byref(good.c), ctypes.byref(q), 4, 1, a, 10, a, 5, 64, 1152,
+                 None, None) == B.EINVAL
+
+
+def test_plan_build_clear_and_writer_counts_checks():
+    m = _meta()
+    fake = 0x100000
+    m.c.d_prefix_pages = fake
+    m.c.d_cur_tokens = fake
+    m.c.d_req_pages = fake
+    p = B.gpb_plan(*([fake] * len(B.PLAN_FIELDS)))
+    f = B.lib.gpb_plan_build_clear
+    assert f(ctypes.byref(m.c), ctypes.byref(p), None, 64, None) == B.EINVAL
+    assert f(ctypes.byref(m.c), ctypes.byref(p), fake, -16, None) == B.EINVAL
+    assert f(ctypes.byref(m.c), ctypes.byref(p), fake + 8, 64, None) == B.EALIGN
+    assert f(ctypes.byref(m.c), ctypes.byref(p), fake, 40, None) == B.EALIGN
+    p.d_prefix_desc = fake + 4   # records are 16-byte aligned
+    assert B.lib.gpb_plan_build(ctypes.byref(m.c), ctypes.byref(p), None) == B.EALIGN
+    # per-writer list sizes on the host: 2 writers, current pages of 64 and
+    # 65 tokens -> pages (64 | 64, 1) dealt 0, 1, 0
+    w = _meta(n_writers=2, staging_cap_pages=4)
+    counts = np.zeros(2, np.int32)
+    assert B.lib.gpb_writer_counts(ctypes.byref(w.c),
+                                   counts.ctypes.data_as(B._I32P)) == B.OK
+    assert counts.tolist() == [64 + 1, 64]
+    assert B.lib.gpb_writer_counts(ctypes.byref(w.c), None) == B.EINVAL
+    bad = _meta(req_pages=[0, 2, 3, 4, 5])
+    assert B.lib.gpb_writer_counts(ctypes.byref(bad.c),
+                                   counts.ctypes.data_as(B._I32P)) == B.EPAGE
+
+
+def test_writer_counts_agree_with_oracle(orc):
+    """The host-side list sizes equal the differences of the oracle's
+    writer_offsets on random multi-writer batches."""
+    for b in pins.random_batches(40, seed=77, n_writers=5, n_pool_entries=2):
+        want = np.diff(oracle.plan_for(b, orc)["writer_offsets"])
+        assert np.array_equal(gpb.writer_counts(gpb.BatchMeta.of(b)), want)
+
+
 def test_group_argument_checks():
     a = 0x100000
     t = B.Sources([(a, 10), (a, 4)])
@@ -296,3 +383,19 @@ def test_host_memory_never_reaches_a_kernel():
 def test_metadata_outside_int32_is_refused():
     with pytest.raises(ValueError):
         gpb.BatchMeta(1, 64, 1152, 16, 1, 1, 4, [2 ** 32 + 1], [0], [1])
+
+
+def test_plan_key_covers_what_a_plan_depends_on():
+    """Two batches share a plan key exactly when their plans are the same:
+    the row size may differ, nothing else (layout, spans, table shape,
+    staging capacity, page ids)."""
+    base = dict(bs=2, page_size=64, row_bytes=1152, n_pool_pages=16, n_pool_entries=1,
+                n_writers=1, staging_cap_pages=4, prefix_pages=[1, 1], cur_tokens=[64, 65],
+                req_pages=[1, 2, 3, 4, 5])
+    key = B.BatchMeta(**base).plan_key()
+    assert B.BatchMeta(**dict(base, row_bytes=144)).plan_key() == key
+    for change in (dict(page_size=32), dict(n_pool_pages=17), dict(n_pool_entries=2),
+                   dict(n_writers=2), dict(staging_cap_pages=5),
+                   dict(prefix_pages=[2, 0]), dict(cur_tokens=[65, 64]),
+                   dict(req_pages=[1, 2, 3, 5, 4])):
+        assert B.BatchMeta(**dict(base, **change)).plan_key() != key, change

@@ -56,7 +56,8 @@ def _read_result(path, b):
     S, T, NCP = np.frombuffer(raw[:12], "<i4")
     bs, npp = b.bs, b.n_pool_pages
     sizes = [bs, 2 * bs, 2 * bs, bs, bs, bs, bs, bs, bs, S, S, S, npp, npp, NCP, T, T, T,
-             T, 4 * bs, S - NCP, NCP, T, NCP, NCP]
+             T, 4 * bs, S - NCP, NCP, T, NCP, NCP, 4 * (S - NCP), 4 * NCP,
+             b.n_writers + 1, T, T, NCP]
     at = 12
     plan = {}
     for name, n in zip(oracle.PLAN_FIELDS, sizes):
@@ -86,7 +87,7 @@ def test_c_consumer_layer_matches_oracle(orc, seed):
             r = subprocess.run([exe, "run", fin, fout], capture_output=True, text=True,
                                timeout=120)
             assert r.returncode == 0, r.stdout + r.stderr
-            assert "slot-list gather, grouped calls and fused fill agree" in r.stdout, r.stdout
+            assert "per-writer scatters and plan build with clear agree" in r.stdout, r.stdout
             plan, staging, dense = _read_result(fout, b)
             want = oracle.plan_for(b, orc)
             for name in oracle.PLAN_FIELDS:

@@ -72,17 +72,21 @@ def _status(r):
 POISON = 0xA5
 
 
-def _run_poisoned(r, n_layers):
-    """The batch as bench.py runs it (plan build, staging clear, then scatter
-    and gather per layer), with the dense half of each of the last two layers
-    filled with a sentinel byte just before that layer runs.  A dense byte the
-    gather fails to write then shows as a mismatch instead of passing on the
-    identical bytes an earlier layer left in the same half."""
+def _run_poisoned(r, n_layers, two_launch=False):
+    """The batch as bench.py runs it (plan build with the staging clear, then
+    each layer's scatter and gather, in one launch or in two), with the dense
+    half of each of the last two layers filled with a sentinel byte just
+    before that layer runs.  A dense byte the gather fails to write then
+    shows as a mismatch instead of passing on the identical bytes an earlier
+    layer left in the same half."""
     r.begin_batch()
     for layer in range(n_layers):
         if layer >= n_layers - 2:
             r.dense[layer % 2].fill_(POISON)
-        r.layer(layer)
+        if two_launch:
+            r.layer_two_launch(layer)
+        else:
+            r.layer(layer)
 
 
 def test_ragged_tails_stay_inside_their_ranges(orc):
@@ -178,15 +182,20 @@ def test_multi_layer_workloads(orc, name):
         torch.cuda.synchronize()
         _check_layer(b, r, layer, want, pools_np, curs_np, orc)
         _say("  layer", layer, "ok")
-    _run_poisoned(r, b.n_layers)
-    torch.cuda.synchronize()
-    for layer in (b.n_layers - 2, b.n_layers - 1):
-        _check_layer(b, r, layer, want, pools_np, curs_np, orc)
-        _say("  layer", layer, "ok")
+    for two in (False, True):
+        _run_poisoned(r, b.n_layers, two_launch=two)
+        torch.cuda.synchronize()
+        for layer in (b.n_layers - 2, b.n_layers - 1):
+            _check_layer(b, r, layer, want, pools_np, curs_np, orc)
+            _say("  layer", layer, "two launches" if two else "one launch", "ok")
     for layer, fused in ((0, False), (1, True)):
         _check_split(b, r, layer, want, pools_np[layer % len(pools_np)],
                      curs_np[layer % len(curs_np)], orc, fused_fill=fused)
         _say("  split layer", layer, "fused fill" if fused else "scatter", "ok")
+    for layer in (2, 3):
+        _check_one_launch(b, r, layer, want, pools_np[layer % len(pools_np)],
+                          curs_np[layer % len(curs_np)], orc)
+        _say("  one-launch layer and fused consume", layer, "ok")
     assert _status(r) == 0
 
 
@@ -224,6 +233,50 @@ def _check_split(batch, r, layer, want_plan, pool_np, cur_np, orc, fused_fill):
         r.pools[k].copy_(torch.from_numpy(pool_np.reshape(r.pools[k].shape)))
 
 
+def _check_one_launch(batch, r, layer, want_plan, pool_np, cur_np, orc):
+    """The layer as two launches (gpb_current_row_scatter, then
+    gpb_compose_gather) and in one (gpb_compose_layer), and the split with
+    its consume half in one launch (prefix records, then
+    gpb_compose_consume), each on a cleared staging half and a poisoned dense
+    half, against the oracle's layer."""
+    dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
+    h = layer % 2
+    for run in (r.layer_two_launch, r.layer_fused):
+        r.staging[h].zero_()
+        r.dense[h].fill_(POISON)
+        run(layer)
+        torch.cuda.synchronize()
+        assert np.array_equal(_host(r.dense_of(layer)), dense), \
+            "%s: dense differs" % run.__name__
+        assert np.array_equal(_host(r.staging_of(layer)), staging), \
+            "%s: staging differs" % run.__name__
+    r.staging[h].zero_()
+    r.dense[h].fill_(POISON)
+    r.gather_prefix(layer)
+    r.consume_fused(layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(r.dense_of(layer)), dense), "fused consume dense differs"
+    assert np.array_equal(_host(r.staging_of(layer)), staging), "fused consume staging differs"
+
+
+def _check_writer_scatters(batch, r, layer, want_plan, pool_np, cur_np, orc):
+    """The scatter run as W writers, each copying its own rows (in its list
+    order) into its own slab, then one gather: staging and dense equal the
+    single scatter's, i.e. the oracle's."""
+    dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
+    h = layer % 2
+    own = r.writer_rows_of(layer)
+    assert [int(x.shape[0]) for x in own] == \
+        np.diff(want_plan["writer_offsets"]).tolist()
+    r.staging[h].zero_()
+    r.dense[h].fill_(POISON)
+    r.scatter_writers(layer, own)
+    r.gather(layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(r.staging_of(layer)), staging), "per-writer staging differs"
+    assert np.array_equal(_host(r.dense_of(layer)), dense), "per-writer dense differs"
+
+
 def _random_case(orc, b, layers=2):
     pool_np, cur_np = pins.tagged_values(b)
     pools = [torch.from_numpy(pool_np).cuda()]
@@ -236,7 +289,123 @@ def _random_case(orc, b, layers=2):
         _check_layer(b, r, layer, want, [pool_np], [cur_np], orc)
     _check_split(b, r, layers, want, pool_np, cur_np, orc, fused_fill=False)
     _check_split(b, r, layers + 1, want, pool_np, cur_np, orc, fused_fill=True)
+    _check_one_launch(b, r, layers, want, pool_np, cur_np, orc)
+    _check_writer_scatters(b, r, layers + 1, want, pool_np, cur_np, orc)
     assert _status(r) == 0
+
+
+@pytest.mark.parametrize("name,consume", [("traced", "fused"), ("opaque", "fused"),
+                                          ("traced", "scatter"), ("medium", "fill"),
+                                          ("traced", "one_stream"), ("opaque", "one_stream"),
+                                          ("medium", "one_stream")])
+def test_layer_ahead_schedule(orc, name, consume):
+    """The whole batch with the layer-ahead prefetch.  On two streams (default
+    priority): layer l + 1's prefix gather runs on a side stream while layer
+    l is consumed on the main stream, ordered only by events.  On one stream
+    ("one_stream"): one launch per layer holds layer l's consume and layer
+    l + 1's prefix gather.  Every layer's dense half is poisoned just before
+    its prefix gather is issued; checked layers are copied out right after
+    their consume (before the half goes to layer l + 2) and compared with the
+    oracle: the first four layers, a middle pair and the last pair."""
+    b = workloads.make_batch(name)
+    L = b.n_layers
+    _say("pipelined", name, consume, "layers", L)
+    pools, curs = workloads.make_values(b, device="cuda")
+    pools_np = [_host(p) for p in pools]
+    curs_np = [_host(c) for c in curs]
+    r = _runner(b, pools, curs)
+    checked = sorted({l for l in (0, 1, 2, 3, L // 2, L // 2 + 1, L - 2, L - 1)
+                      if 0 <= l < L})
+    snaps = {}
+    stag = {}
+
+    def poison(l, side):
+        with torch.cuda.stream(side):
+            r.dense[l % 2].fill_(POISON)
+
+    def keep(l, stream):
+        if l in checked:
+            with torch.cuda.stream(stream):
+                snaps[l] = r.dense_of(l).clone()
+                stag[l] = r.staging_of(l).clone()
+
+    main = torch.cuda.current_stream()
+    if consume == "one_stream":
+        r.run_layer_ahead(L, main, before_prefetch=poison, after_consume=keep)
+    else:
+        side = torch.cuda.Stream()
+        r.run_pipelined(L, main, side, consume=consume, before_prefetch=poison,
+                        after_consume=keep)
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    for l in checked:
+        k = l % len(pools_np)
+        dense, staging = _oracle_layer(b, want, pools_np[k], curs_np[k], orc)
+        got = _host(snaps[l])
+        if not np.array_equal(got, dense):
+            bad_rows = np.nonzero((got != dense).any(axis=1))[0]
+            raise AssertionError("pipelined layer %d: %d dense rows differ, first %s"
+                                 % (l, len(bad_rows), bad_rows[:8].tolist()))
+        assert np.array_equal(_host(stag[l]), staging), "pipelined layer %d staging" % l
+        _say("  layer", l, "ok")
+    assert _status(r) == 0
+
+
+@pytest.mark.parametrize("name", ["multi_source", "medium"])
+def test_writer_scatters_full_size(orc, name):
+    """The full-size batch with the scatter split over its writers (8 on the
+    multi-source table): byte-exact staging and dense."""
+    b = workloads.make_batch(name)
+    pools, curs = workloads.make_values(b, device="cuda")
+    r = _runner(b, pools, curs)
+    r.begin_batch()
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    _check_writer_scatters(b, r, 0, want, _host(pools[0]), _host(curs[0]), orc)
+    _check_one_launch(b, r, 1, want, _host(pools[0]), _host(curs[0]), orc)
+    assert _status(r) == 0
+
+
+def test_shared_plan_must_match_the_batch(orc):
+    """A twin format may share a plan only if the batch metadata, the table
+    layout and the staging capacity are the same; the row size may differ."""
+    gpb = _gpb()
+    b = workloads.make_batch("tiny")
+    pools, curs = workloads.make_values(b, device="cuda")
+    tok = _runner(b, pools, curs)
+    rb = 144
+    ipools, icurs = workloads.make_values(b, device="cuda", row_bytes=rb, value_kind="bytes")
+    ok = gpb.BatchMeta(b.bs, b.page_size, rb, b.n_pool_pages, b.n_pool_entries, b.n_writers,
+                       b.staging_cap_pages, b.prefix_pages, b.cur_tokens, b.req_pages)
+    gpb.ComposeRunner(ok, ipools, icurs, plan=tok.plan)
+    bad = gpb.BatchMeta(b.bs, b.page_size, rb, b.n_pool_pages, b.n_pool_entries,
+                        b.n_writers, b.staging_cap_pages + 1, b.prefix_pages, b.cur_tokens,
+                        b.req_pages)
+    with pytest.raises(ValueError):
+        gpb.ComposeRunner(bad, ipools, icurs, plan=tok.plan)
+
+
+def test_records_out_of_range_are_skipped(orc):
+    """A record whose slot is outside the dense buffer is skipped and
+    flagged; the others are gathered."""
+    gpb = _gpb()
+    PS, RB = 2, 32
+    rng = np.random.default_rng(14)
+    pool_np = rng.integers(1, 256, (6 * PS, RB), dtype=np.uint8)
+    pool = torch.from_numpy(pool_np).cuda()
+    dense = torch.full((4 * PS, RB), 0x33, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rec = torch.tensor([[2, 0, 3, 0], [9, 0, 1, 0], [-1, 0, 2, 0], [0, 0, 1, 0],
+                        [3, 0, -1, 0]], dtype=torch.int32, device="cuda")
+    gpb.compose_gather_records(dense, [(pool, 6)], rec, 5, 4, PS, RB, status)
+    torch.cuda.synchronize()
+    h = _host(dense).reshape(4, PS, RB)
+    want = np.full((4, PS, RB), 0x33, np.uint8)
+    want[2] = pool_np[3 * PS:4 * PS]
+    want[0] = pool_np[1 * PS:2 * PS]
+    want[3] = 0
+    assert np.array_equal(h, want)
+    assert int(status.item()) == gpb.STATUS_BAD_DESCRIPTOR
 
 
 @pytest.mark.parametrize("seed", range(4))
