@@ -4,10 +4,15 @@
  * Per batch, gpb_plan_build turns host batch metadata into the layer-invariant
  * plan: slot spans, the page inverse and its staging-remapped twin, gather
  * descriptors (owner, src), per-token staging rows and mixed_locs, and the
- * ragged int32 descriptors.  Per layer, gpb_current_row_scatter writes the
- * current token rows into the zeroed staging span and gpb_compose_gather fills
- * the slot-dense KV buffer one page per slot from a pointer table of source
- * arenas [pool entries || staging slabs].
+ * ragged int32 descriptors (gpb_plan_build_clear also zeroes the staging
+ * region in the same launches).  Per layer, gpb_current_row_scatter writes
+ * the current token rows into the zeroed staging span and gpb_compose_gather
+ * fills the slot-dense KV buffer one page per slot from a pointer table of
+ * source arenas [pool entries || staging slabs]; gpb_compose_layer does both
+ * in one launch.  The layer-ahead split gathers a layer's prefix pages
+ * early (gpb_compose_gather_records) and its current pages at consume time
+ * (gpb_compose_consume), or layer l's consume together with layer l + 1's
+ * prefix pages (gpb_compose_layer_ahead).
  *
  * Where the method comes from (commit pages of the sglang fork, cited by the
  * page's commit hash and the commit's subject):
