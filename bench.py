@@ -66,6 +66,7 @@ def _args():
 # include from the library (plan kernels and host entry points elsewhere do
 # not change the gather's traffic)
 DIGEST_FILES = ("gather_plan_build_amd/csrc/compose.hip",
+                "gather_plan_build_amd/csrc/layer_unit.h",
                 "gather_plan_build_amd/csrc/buffer_io.h",
                 "gather_plan_build_amd/csrc/gpb_common.h")
 
@@ -267,7 +268,8 @@ def _short(name):
     kept (they tell the gather from the slot-list gather, the scatter from the
     fused fill)."""
     import re
-    for key in ("k_compose_layer", "k_compose_gather", "k_row_scatter", "k_gather_groups",
+    for key in ("k_compose_layer", "k_layer_groups", "k_compose_gather", "k_row_scatter",
+                "k_gather_groups",
                 "k_scatter_groups", "k_fill_zero", "k_plan_scan_fill", "k_plan_slots",
                 "k_plan_tokens", "copyBuffer"):
         if key in name:
@@ -326,7 +328,9 @@ def summarize_extras(trace_dir, workload="traced"):
     lines = ["# rocprofv3 kernel statistics, %s workload with the extras "
              "(bench.py default run)" % workload,
              "# command: " + cmd,
-             "# LIST = slot-list gather (prefetch split), FILL = fused fill, "
+             "# k_compose_gather<64,1,M>: M = 0 all slots, 1 slot list, 2 records (split "
+             "halves); k_row_scatter<64,1,FILL,SROWS>: FILL = fused fill; "
+             "k_compose_layer<64,SROWS>: one-launch layer, consume and layer-ahead launches; "
              "*_groups = token KV and index twin in one launch",
              "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
@@ -653,7 +657,9 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
         sep_ms = region(lambda: [(runner.layer(l, stream), twin.layer(l, stream))
                                  for l in range(L)], 2 * L) / L
         both_ms = region(lambda: [gpb.layer_groups([runner, twin], l, stream)
-                                  for l in range(L)], 2 * L) / L
+                                  for l in range(L)], L) / L
+        both2_ms = region(lambda: [gpb.layer_groups_two_launch([runner, twin], l, stream)
+                                   for l in range(L)], 2 * L) / L
         both_b = runner.algorithmic_bytes_per_layer() + tb
         out["index_twin"] = {"row_bytes": rb, "us_per_layer": round(t_ms * 1e3, 2),
                              "algorithmic_bytes_per_layer": tb,
@@ -663,7 +669,11 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
                              "two_launch_us_per_layer": round(t2_ms * 1e3, 2),
                              "token_and_twin_separate_us": round(sep_ms * 1e3, 2),
                              "token_and_twin_grouped_us": round(both_ms * 1e3, 2),
-                             "grouped_gbs": round(both_b / (both_ms * 1e-3) / 1e9, 1)}
+                             "grouped_gbs": round(both_b / (both_ms * 1e-3) / 1e9, 1),
+                             "grouped_pct_of_peak": round(100.0 * both_b / (both_ms * 1e-3)
+                                                          / 1e9 / HBM_PEAK_GBS, 2),
+                             "token_and_twin_grouped_two_launch_us": round(both2_ms * 1e3,
+                                                                           2)}
         assert int(twin.status.item()) == 0
         del ipools, icurs, twin
 

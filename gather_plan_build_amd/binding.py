@@ -69,6 +69,12 @@ class gpb_gather_group(ctypes.Structure):
                 ("row_bytes", ctypes.c_int32)]
 
 
+class gpb_layer_group(ctypes.Structure):
+    _fields_ = [("d_dense", ctypes.c_void_p), ("table", ctypes.POINTER(gpb_sources)),
+                ("d_staging", ctypes.c_void_p), ("n_staging_rows", ctypes.c_int64),
+                ("d_cur_rows", ctypes.c_void_p), ("row_bytes", ctypes.c_int32)]
+
+
 def _hip_runtimes():
     """Distinct libamdhip64 files mapped into this process."""
     found = set()
@@ -121,6 +127,9 @@ def _load(path):
                                                    i32, vp, vp]
     lib.gpb_compose_gather_groups.argtypes = [ctypes.POINTER(gpb_gather_group), i32, vp, vp,
                                               i32, i32, vp, vp]
+    lib.gpb_compose_layer_groups.argtypes = [ctypes.POINTER(gpb_layer_group), i32,
+                                             ctypes.POINTER(gpb_plan), i32, i32, i32, i32,
+                                             vp, vp]
     lib.gpb_strerror.argtypes = [ctypes.c_int]
     lib.gpb_strerror.restype = ctypes.c_char_p
     for f in EXPORTS:
@@ -134,7 +143,7 @@ EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_plan_build_clear",
            "gpb_compose_gather", "gpb_compose_gather_slots", "gpb_compose_gather_records",
            "gpb_compose_layer", "gpb_compose_consume", "gpb_compose_layer_ahead",
            "gpb_current_row_fill", "gpb_current_row_scatter_groups",
-           "gpb_compose_gather_groups", "gpb_strerror")
+           "gpb_compose_gather_groups", "gpb_compose_layer_groups", "gpb_strerror")
 
 lib = _load(LIB_PATH)
 
@@ -448,3 +457,16 @@ def compose_gather_groups(groups, owner, src, n_slots, page_rows, status=None, s
                                          _stream(stream)),
            "gpb_compose_gather_groups")
 
+
+def compose_layer_groups(groups, plan, n_slots, n_cur_pages, n_rows, page_rows, status=None,
+                         stream=None):
+    """One launch composing one layer of every group: groups = [(dense, Sources, staging,
+    n_staging_rows, cur_rows, row_bytes), ...] on one plan (a Plan)."""
+    keep = [g[1] if isinstance(g[1], Sources) else Sources(g[1]) for g in groups]
+    arr = (gpb_layer_group * max(len(groups), 1))(
+        *[gpb_layer_group(_ptr(d), ctypes.pointer(t.c), _ptr(st), int(n), _ptr(cur), int(rb))
+          for (d, _, st, n, cur, rb), t in zip(groups, keep)])
+    _check(lib.gpb_compose_layer_groups(arr, len(groups), ctypes.byref(plan.c), int(n_slots),
+                                        int(n_cur_pages), int(n_rows), int(page_rows),
+                                        _ptr(status), _stream(stream)),
+           "gpb_compose_layer_groups")

@@ -31,6 +31,7 @@
 
 #include "buffer_io.h"
 #include "gpb_common.h"
+#include "layer_unit.h"
 
 #ifndef GPB_GATHER_BLOCK
 #define GPB_GATHER_BLOCK 64    // lanes per gather workgroup (one wave64)
@@ -48,15 +49,8 @@
 namespace gpb {
 namespace {
 
-constexpr int kScalarRows = 4;  // staging rows a scatter workgroup may fetch as scalars
 
-struct SrcTable {
-  const uint8_t *base[GPB_MAX_SOURCES];
-  int64_t n_pages[GPB_MAX_SOURCES];
-  int32_t n;
-};
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef ArenaTable<GPB_MAX_SOURCES> SrcTable;
 
 // How a gather workgroup finds its page: dense slot k (owner[k], src[k]),
 // the k-th entry of a slot list (slots[k], then owner/src of that slot), or
@@ -108,31 +102,12 @@ __global__ __launch_bounds__(B) void k_compose_gather(
     atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
 }
 
-// One launch for a whole layer: the current-row scatter and the gather of
-// every dense slot.  The units are 1 KiB of a page, one wave each: first the
-// current pages' units (record k of the current records, tokens
-// tok0[k] .. tok0[k] + ntok[k] - 1 on it), then the prefix pages' units.  A
-// current unit first copies the current-row chunks that fall in its KiB of
-// the page into staging (the scatter: token t to staging row rows[t]), then
-// reads its KiB back from staging through its gather record and stores it
-// into the dense page, as the gather does.  Through a valid plan the chunk a
-// lane reads back is the chunk that lane wrote, so the lane's own program
-// order orders the read after the write; rows past the page's tokens read
-// the zeros the per-batch clear left.  `staging` is deliberately not
-// __restrict__: the table's staging entries alias it, and the read-back must
-// stay behind the write.  The staging stores and the read-back carry the
-// plain cache policy, so the read-back is served by the L2 the wave just
-// wrote to (the two-launch path's scatter writes through instead, since its
-// reader is another kernel); on the traced workload this makes the one
-// launch 6 us per layer faster than the scatter and gather launched apart.
-//
-// Prefix pages go to dense_pre, current pages to dense: the same buffer for
-// one layer, or the next layer's dense buffer for the prefix pages when the
-// launch is layer l's consume together with layer l + 1's prefetch (the
-// table then lists layer l + 1's pool entries and layer l's staging slabs).
-//
-// With SROWS (rows of at least 21 chunks) a unit spans at most kScalarRows
-// rows, whose staging rows are fetched once with scalar loads.
+// One launch for a whole layer (layer_unit.h): the current pages' units
+// first, then the prefix pages' units.  Prefix pages go to dense_pre, current
+// pages to dense: the same buffer for one layer, or the next layer's dense
+// buffer for the prefix pages when the launch is layer l's consume together
+// with layer l + 1's prefetch (the table then lists layer l + 1's pool
+// entries and layer l's staging slabs).
 template <int B, bool SROWS>
 __global__ __launch_bounds__(B) void k_compose_layer(
     uint8_t *dense, uint8_t *dense_pre, SrcTable tbl, const int32_t *__restrict__ pre_desc,
@@ -144,54 +119,9 @@ __global__ __launch_bounds__(B) void k_compose_layer(
   const bool is_cur = static_cast<int>(blockIdx.x) < n_cur_units;
   const int u = is_cur ? blockIdx.x : blockIdx.x - n_cur_units;
   const int k = u / parts;
-  const int part = u - k * parts;
-  const i32x4 rec = reinterpret_cast<const i32x4 *>(is_cur ? cur_desc : pre_desc)[k];
-  const int slot = rec.x, e = rec.y, p = rec.z;
-  if (slot < 0 || slot >= n_slots) {
-    if (status && part == 0 && threadIdx.x == 0) atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
-    return;
-  }
-  const int c = part * B + threadIdx.x;  // 16-byte chunk of the page
-  const uint32_t off = static_cast<uint32_t>(c) * 16u;
-  if (is_cur) {
-    const int t0 = tok0[k], nt = ntok[k];
-    const int j = c / row_chunks;  // row of the page
-    const int oc = c - j * row_chunks;
-    const int t = t0 + j;
-    const bool live = j < nt && off < static_cast<uint32_t>(page_bytes);
-    const bool in_rows = live && t >= 0 && t < n_rows;
-    int d;
-    if (SROWS) {
-      const int j0 = part * B / row_chunks;  // first row of the unit (uniform)
-      int srow[kScalarRows];
-#pragma unroll
-      for (int q = 0; q < kScalarRows; ++q)
-        srow[q] = rows[min(max(t0 + j0 + q, 0), n_rows - 1)];
-      d = srow[kScalarRows - 1];
-#pragma unroll
-      for (int q = kScalarRows - 2; q >= 0; --q) d = j - j0 == q ? srow[q] : d;
-    } else {
-      d = rows[in_rows ? t : 0];
-    }
-    const bool ok = in_rows && d >= 0 && d < n_staging_rows;
-    const __amdgpu_buffer_rsrc_t rc = rsrc(cur, n_rows * row_chunks * 16);
-    const __amdgpu_buffer_rsrc_t rst = rsrc(staging, staging_bytes);
-    const u32x4 v = ld16(rc, in_rows ? static_cast<uint32_t>(t * row_chunks + oc) * 16u
-                                     : kDropOffset);
-    st16_staged(v, rst, ok ? static_cast<uint32_t>(d * row_chunks + oc) * 16u : kDropOffset);
-    if (live && !ok && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
-  }
-  const bool sentinel = (e < 0) || (p < 0);
-  const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
-  const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
-  const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
-  const __amdgpu_buffer_rsrc_t rd =
-      rsrc((is_cur ? dense : dense_pre) + static_cast<int64_t>(slot) * page_bytes, page_bytes);
-  // a current page's bytes were just written by this very wave: read them
-  // back through the cache; pool pages are streamed
-  st16_dense(is_cur ? ld16_staged(rs, off) : ld16(rs, off), rd, off);
-  if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
-    atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+  layer_unit<B, SROWS>(tbl, dense, dense_pre, is_cur, k, u - k * parts, pre_desc, cur_desc,
+                       tok0, ntok, staging, staging_bytes, n_staging_rows, rows, cur, n_rows,
+                       row_chunks, n_slots, page_bytes, status);
 }
 
 // Flat over (row, chunk) of the current rows: lane g of the grid handles

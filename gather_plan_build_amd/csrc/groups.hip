@@ -14,6 +14,7 @@
 // instead of paying their own.
 #include "buffer_io.h"
 #include "gpb_common.h"
+#include "layer_unit.h"
 
 namespace gpb {
 namespace {
@@ -95,8 +96,131 @@ __global__ __launch_bounds__(kUnitLanes) void k_scatter_groups(
   if (live && !ok && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
 }
 
+// The one-launch layer (layer_unit.h) for every group: first the current
+// pages' units of all groups, then their prefix pages' units, each group's
+// units consecutive.  The groups share the plan's records, token ranges and
+// staging rows; each has its own dense buffer, staging, current rows, table
+// and row size.
+struct LayerGroupArgs {
+  uint8_t *dense, *staging;
+  const uint8_t *cur;
+  ArenaTable<GPB_MAX_GROUP_SOURCES> tbl;
+  int32_t staging_bytes, n_staging_rows, row_chunks, page_bytes, parts;
+  int32_t srows;                 // staging rows fetched as scalars
+  int32_t cur_begin, pre_begin;  // first unit of the group's current / prefix units
+};
+struct LayerGroupsArgs {
+  LayerGroupArgs g[GPB_MAX_GROUPS];
+  int32_t n;
+  int32_t n_cur_units;  // units of every group's current pages, which come first
+};
+
+__global__ __launch_bounds__(kUnitLanes) void k_layer_groups(
+    LayerGroupsArgs G, const int32_t *__restrict__ pre_desc,
+    const int32_t *__restrict__ cur_desc, const int32_t *__restrict__ tok0,
+    const int32_t *__restrict__ ntok, const int32_t *__restrict__ rows, int32_t n_rows,
+    int32_t n_slots, int32_t *status) {
+  const int unit = blockIdx.x;
+  const bool is_cur = unit < G.n_cur_units;
+  int gi = 0;
+#pragma unroll
+  for (int k = 1; k < GPB_MAX_GROUPS; ++k)
+    if (k < G.n && unit >= (is_cur ? G.g[k].cur_begin : G.g[k].pre_begin)) gi = k;
+  const LayerGroupArgs &gr = G.g[gi];
+  const int u = unit - (is_cur ? gr.cur_begin : gr.pre_begin);
+  const int k = u / gr.parts;
+  if (gr.srows)
+    layer_unit<kUnitLanes, true>(gr.tbl, gr.dense, gr.dense, is_cur, k, u - k * gr.parts,
+                                 pre_desc, cur_desc, tok0, ntok, gr.staging, gr.staging_bytes,
+                                 gr.n_staging_rows, rows, gr.cur, n_rows, gr.row_chunks,
+                                 n_slots, gr.page_bytes, status);
+  else
+    layer_unit<kUnitLanes, false>(gr.tbl, gr.dense, gr.dense, is_cur, k, u - k * gr.parts,
+                                  pre_desc, cur_desc, tok0, ntok, gr.staging, gr.staging_bytes,
+                                  gr.n_staging_rows, rows, gr.cur, n_rows, gr.row_chunks,
+                                  n_slots, gr.page_bytes, status);
+}
+
 }  // namespace
 }  // namespace gpb
+
+extern "C" int gpb_compose_layer_groups(const gpb_layer_group *groups, int32_t n_groups,
+                                        const gpb_plan *plan, int32_t n_slots,
+                                        int32_t n_cur_pages, int32_t n_rows, int32_t page_rows,
+                                        int32_t *d_status, void *stream) {
+  using namespace gpb;
+  if (!groups || !plan || n_groups < 1 || n_groups > GPB_MAX_GROUPS || n_slots < 0 ||
+      page_rows < 1 || n_cur_pages < 0 || n_cur_pages > n_slots || n_rows < 0 ||
+      n_cur_pages > n_rows)
+    return GPB_EINVAL;
+  if (d_status && !aligned(d_status, 4)) return GPB_EALIGN;
+  const int32_t n_prefix = n_slots - n_cur_pages;
+  LayerGroupsArgs G;
+  G.n = n_groups;
+  for (int k = 0; k < GPB_MAX_GROUPS; ++k) G.g[k] = LayerGroupArgs{};
+  int64_t units = 0;
+  // first pass: each group's geometry and its current units; second: prefix
+  for (int k = 0; k < n_groups; ++k) {
+    const gpb_layer_group &q = groups[k];
+    if (!q.table || q.table->n < 1 || q.table->n > GPB_MAX_GROUP_SOURCES || q.row_bytes < 1 ||
+        q.n_staging_rows < 0)
+      return GPB_EINVAL;
+    if (q.row_bytes % 16 != 0) return GPB_EALIGN;
+    if (q.n_staging_rows > INT32_MAX) return GPB_ERANGE;
+    const int64_t page_bytes = static_cast<int64_t>(page_rows) * q.row_bytes;
+    if (page_bytes > INT32_MAX - (1 << 20)) return GPB_ERANGE;
+    LayerGroupArgs &a = G.g[k];
+    a.tbl.n = q.table->n;
+    for (int e = 0; e < q.table->n; ++e) {
+      if (q.table->n_pages[e] < 0) return GPB_EINVAL;
+      if (q.table->n_pages[e] > 0 && !q.table->base[e]) return GPB_EINVAL;
+      if (!aligned(q.table->base[e], 16)) return GPB_EALIGN;
+      a.tbl.base[e] = static_cast<const uint8_t *>(q.table->base[e]);
+      a.tbl.n_pages[e] = q.table->n_pages[e];
+    }
+    const int64_t row_chunks = q.row_bytes / 16;
+    const int64_t cur_bytes = static_cast<int64_t>(n_rows) * q.row_bytes;
+    const int64_t staging_bytes = q.n_staging_rows * q.row_bytes;
+    if (cur_bytes > INT32_MAX || staging_bytes > INT32_MAX) return GPB_ERANGE;
+    if (n_slots == 0) continue;
+    if (!q.d_dense || (n_cur_pages > 0 && (!q.d_staging || !q.d_cur_rows))) return GPB_EINVAL;
+    if (!aligned(q.d_dense, 16) || !aligned(q.d_staging, 16) || !aligned(q.d_cur_rows, 16))
+      return GPB_EALIGN;
+    a.dense = static_cast<uint8_t *>(q.d_dense);
+    a.staging = static_cast<uint8_t *>(q.d_staging);
+    a.cur = static_cast<const uint8_t *>(q.d_cur_rows);
+    a.staging_bytes = static_cast<int32_t>(staging_bytes);
+    a.n_staging_rows = static_cast<int32_t>(q.n_staging_rows);
+    a.row_chunks = static_cast<int32_t>(row_chunks);
+    a.page_bytes = static_cast<int32_t>(page_bytes);
+    a.parts = static_cast<int32_t>(ceil_div64(page_bytes / 16, kUnitLanes));
+    // a unit of kUnitLanes chunks touches at most 2 + (kUnitLanes - 2) / row_chunks rows
+    a.srows = 2 + (kUnitLanes - 2) / row_chunks <= kScalarRows;
+    a.cur_begin = static_cast<int32_t>(units);
+    units += static_cast<int64_t>(a.parts) * n_cur_pages;
+    if (units > INT32_MAX) return GPB_ERANGE;
+  }
+  if (n_slots == 0) return GPB_OK;
+  G.n_cur_units = static_cast<int32_t>(units);
+  for (int k = 0; k < n_groups; ++k) {
+    G.g[k].pre_begin = static_cast<int32_t>(units);
+    units += static_cast<int64_t>(G.g[k].parts) * n_prefix;
+    if (units > INT32_MAX) return GPB_ERANGE;
+  }
+  if ((n_prefix > 0 && !plan->d_prefix_desc) ||
+      (n_cur_pages > 0 && (!plan->d_current_desc || !plan->d_cur_page_token0 ||
+                           !plan->d_cur_page_ntok || !plan->d_staging_rows)))
+    return GPB_EINVAL;
+  if (!aligned(plan->d_prefix_desc, 16) || !aligned(plan->d_current_desc, 16) ||
+      !aligned(plan->d_cur_page_token0, 4) || !aligned(plan->d_cur_page_ntok, 4) ||
+      !aligned(plan->d_staging_rows, 4))
+    return GPB_EALIGN;
+  if (units == 0) return GPB_OK;
+  return launch(k_layer_groups, dim3(static_cast<uint32_t>(units)), dim3(kUnitLanes),
+                as_stream(stream), G, plan->d_prefix_desc, plan->d_current_desc,
+                plan->d_cur_page_token0, plan->d_cur_page_ntok, plan->d_staging_rows, n_rows,
+                n_slots, d_status);
+}
 
 extern "C" int gpb_current_row_scatter_groups(const gpb_row_group *groups, int32_t n_groups,
                                               const int32_t *d_staging_rows, int32_t n_rows,

@@ -1,0 +1,105 @@
+// The unit of the one-launch layer: 1 KiB of one dense page, one wave, for
+// the single-format kernel (compose.hip) and the grouped one (groups.hip).
+#pragma once
+
+#include "buffer_io.h"
+#include "gpb_common.h"
+
+namespace gpb {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScalarRows = 4;  // staging rows a workgroup may fetch as scalars
+
+// Source arenas of a pointer table, passed by value in the kernel arguments:
+// arena e starts at base[e] and holds n_pages[e] whole pages.
+template <int N>
+struct ArenaTable {
+  const uint8_t *base[N];
+  int64_t n_pages[N];
+  int32_t n;
+};
+
+// One unit of the layer's scatter and gather (page d63fbd4, commit "current
+// rows written straight into staging": the current rows go into cleared
+// staging, then every dense slot is gathered from the table of pool entries
+// and staging slabs).  The unit serves record k of the current records
+// (is_cur: a current page, tokens tok0[k] .. tok0[k] + ntok[k] - 1 on it) or
+// of the prefix records, and chunk `part * B + lane` of its page.
+//
+// A current unit first copies the current-row chunks that fall in its KiB
+// of the page into staging (the scatter: token t to staging row rows[t]),
+// then reads its KiB back from staging through its gather record and stores
+// it into the dense page, as the gather does.  Through a valid plan the
+// chunk a lane reads back is the chunk that lane wrote, so the lane's own
+// program order orders the read after the write; rows past the page's
+// tokens read the zeros the per-batch clear left.  `staging` is deliberately
+// not __restrict__: the table's staging entries alias it, and the read-back
+// must stay behind the write.  The staging stores and the read-back carry
+// the plain cache policy: the store completes in L2 instead of writing
+// through to memory, so the read-back does not wait on a trip to memory
+// (part of it is served by L2 itself).  The two-launch path's scatter
+// writes through instead, since its reader is another kernel.
+//
+// A prefix unit copies its KiB of a pool page into dense_pre; a current unit
+// stores into dense.  With SROWS (rows of at least 21 chunks) a unit spans
+// at most kScalarRows rows, whose staging rows are fetched once with scalar
+// loads.
+template <int B, bool SROWS, typename Table>
+__device__ __forceinline__ void layer_unit(
+    const Table &tbl, uint8_t *dense, uint8_t *dense_pre, bool is_cur, int k, int part,
+    const int32_t *__restrict__ pre_desc, const int32_t *__restrict__ cur_desc,
+    const int32_t *__restrict__ tok0, const int32_t *__restrict__ ntok, uint8_t *staging,
+    int32_t staging_bytes, int32_t n_staging_rows, const int32_t *__restrict__ rows,
+    const uint8_t *__restrict__ cur, int32_t n_rows, int32_t row_chunks, int32_t n_slots,
+    int32_t page_bytes, int32_t *status) {
+  const i32x4 rec = reinterpret_cast<const i32x4 *>(is_cur ? cur_desc : pre_desc)[k];
+  const int slot = rec.x, e = rec.y, p = rec.z;
+  if (slot < 0 || slot >= n_slots) {
+    if (status && part == 0 && threadIdx.x == 0) atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+    return;
+  }
+  const int c = part * B + threadIdx.x;  // 16-byte chunk of the page
+  const uint32_t off = static_cast<uint32_t>(c) * 16u;
+  if (is_cur) {
+    const int t0 = tok0[k], nt = ntok[k];
+    const int j = c / row_chunks;  // row of the page
+    const int oc = c - j * row_chunks;
+    const int t = t0 + j;
+    const bool live = j < nt && off < static_cast<uint32_t>(page_bytes);
+    const bool in_rows = live && t >= 0 && t < n_rows;
+    int d;
+    if (SROWS) {
+      const int j0 = part * B / row_chunks;  // first row of the unit (uniform)
+      int srow[kScalarRows];
+#pragma unroll
+      for (int q = 0; q < kScalarRows; ++q)
+        srow[q] = rows[min(max(t0 + j0 + q, 0), n_rows - 1)];
+      d = srow[kScalarRows - 1];
+#pragma unroll
+      for (int q = kScalarRows - 2; q >= 0; --q) d = j - j0 == q ? srow[q] : d;
+    } else {
+      d = rows[in_rows ? t : 0];
+    }
+    const bool ok = in_rows && d >= 0 && d < n_staging_rows;
+    const __amdgpu_buffer_rsrc_t rc = rsrc(cur, n_rows * row_chunks * 16);
+    const __amdgpu_buffer_rsrc_t rst = rsrc(staging, staging_bytes);
+    const u32x4 v = ld16(rc, in_rows ? static_cast<uint32_t>(t * row_chunks + oc) * 16u
+                                     : kDropOffset);
+    st16_staged(v, rst, ok ? static_cast<uint32_t>(d * row_chunks + oc) * 16u : kDropOffset);
+    if (live && !ok && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
+  }
+  const bool sentinel = (e < 0) || (p < 0);
+  const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
+  const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
+  const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rd =
+      rsrc((is_cur ? dense : dense_pre) + static_cast<int64_t>(slot) * page_bytes, page_bytes);
+  // a current page's bytes were just written by this very wave: read them
+  // back through the cache; pool pages are streamed
+  st16_dense(is_cur ? ld16_staged(rs, off) : ld16(rs, off), rd, off);
+  if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
+    atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+}
+
+}  // namespace gpb

@@ -333,8 +333,20 @@ class ComposeRunner:
 
 def layer_groups(runners, layer, stream=None):
     """One layer for several row formats sharing one plan (the token KV and
-    its index-key twin): one scatter launch and one gather launch for all of
-    them."""
+    its index-key twin) in one launch for all of them."""
+    r0 = runners[0]
+    if any(r.plan is not r0.plan for r in runners[1:]):
+        raise ValueError("grouped formats must share one plan")
+    h = layer % PARITY
+    B.compose_layer_groups(
+        [(r.dense[h], r.tables[(layer % len(r.pools), h)], r.staging[h], r.staging_rows_total,
+          r.curs[layer % len(r.curs)], r.rb) for r in runners],
+        r0.plan, r0.S, r0.plan.NCP, r0.T, r0.ps, r0.status, stream)
+
+
+def layer_groups_two_launch(runners, layer, stream=None):
+    """One layer for several row formats sharing one plan: one scatter launch
+    and one gather launch for all of them."""
     r0 = runners[0]
     if any(r.plan is not r0.plan for r in runners[1:]):
         raise ValueError("grouped formats must share one plan")

@@ -444,6 +444,31 @@ int gpb_compose_gather_groups(const gpb_gather_group *groups, int32_t n_groups,
                               int32_t n_slots, int32_t page_rows, int32_t *d_status,
                               void *stream);
 
+typedef struct gpb_layer_group {    /* one format's one-launch layer        */
+  void *d_dense;                    /* n_slots pages of page_rows*row_bytes */
+  const gpb_sources *table;         /* n <= GPB_MAX_GROUP_SOURCES: pool
+                                       entries, then the slabs carved from
+                                       d_staging                           */
+  void *d_staging;                  /* n_staging_rows rows, zero where the
+                                       plan writes no row                  */
+  int64_t n_staging_rows;
+  const void *d_cur_rows;           /* n_rows rows of row_bytes            */
+  int32_t row_bytes;                /* multiple of 16                      */
+} gpb_layer_group;
+
+/* gpb_compose_layer for every group (same plan, n_slots, n_cur_pages,
+ * n_rows and page_rows), one launch: the current pages of every group first,
+ * then their prefix pages, so the formats share one launch's ramp.  The
+ * result is the one gpb_compose_layer gives per group; the requirements are
+ * its requirements, per group.  Errors as gpb_compose_layer for any group,
+ * plus GPB_EINVAL for n_groups outside 1..GPB_MAX_GROUPS or a table of more
+ * than GPB_MAX_GROUP_SOURCES entries, and GPB_ERANGE past 2^31 workgroups in
+ * total. */
+int gpb_compose_layer_groups(const gpb_layer_group *groups, int32_t n_groups,
+                             const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
+                             int32_t n_rows, int32_t page_rows, int32_t *d_status,
+                             void *stream);
+
 /* Static, human-readable name of a gpb_status value. */
 const char *gpb_strerror(int status);
 

@@ -186,12 +186,20 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
   for (int w = 0; w < b->n_writers; w++)
     t2.base[b->n_pool_entries + w] =
         (uint8_t *)d_stag2 + (size_t)w * b->staging_cap_pages * PS * RB;
-  for (int pass = 0; pass < 3; pass++) {
+  for (int pass = 0; pass < 4; pass++) {
     CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
     HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
     if (pass == 0) {
       CHECK(gpb_compose_layer(d_dense2, &t2, p, S, NCP, d_stag2, (int64_t)stag_rows, d_cur, T,
                               b->page_size, b->row_bytes, d_status, st));
+    } else if (pass == 3) {
+      /* the grouped one-launch layer with a single group */
+      gpb_layer_group lg = {d_dense2, &t2, d_stag2, (int64_t)stag_rows, d_cur, b->row_bytes};
+      if (t2.n <= GPB_MAX_GROUP_SOURCES)
+        CHECK(gpb_compose_layer_groups(&lg, 1, p, S, NCP, T, b->page_size, d_status, st));
+      else
+        CHECK(gpb_compose_layer(d_dense2, &t2, p, S, NCP, d_stag2, (int64_t)stag_rows, d_cur,
+                                T, b->page_size, b->row_bytes, d_status, st));
     } else if (pass == 2) {
       /* this layer's consume and the "next" layer's prefix pages, here into
        * the same buffer's prefix slots through a separate pointer */
@@ -208,7 +216,8 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
     if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB) ||
         !same_device_bytes(d_dense2, d_dense, dense_bytes)) {
       fprintf(stderr, "%s differs from the two-call layer\n",
-              pass == 0 ? "one-launch layer" : pass == 1 ? "fused consume" : "layer ahead");
+              pass == 0 ? "one-launch layer" : pass == 1 ? "fused consume"
+              : pass == 2 ? "layer ahead" : "grouped one-launch layer");
       return 11;
     }
   }
@@ -274,8 +283,8 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
   HCHECK(hipFree(d_stag2));
   HCHECK(hipFree(d_pool2));
   printf("c consumer: slot-list and record gathers, grouped calls, fused fill, one-launch "
-         "layer, fused consume, layer ahead, per-writer scatters and plan build with clear "
-         "agree\n");
+         "layer (single and grouped), fused consume, layer ahead, per-writer scatters and "
+         "plan build with clear agree\n");
   return 0;
 }
 

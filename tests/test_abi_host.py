@@ -209,6 +209,37 @@ def test_one_launch_layer_argument_checks():
                  None, None) == B.EINVAL
 
 
+def test_layer_groups_argument_checks():
+    f = B.lib.gpb_compose_layer_groups
+    a = 0x100000
+    t = B.Sources([(a, 10), (a, 4)])
+    p = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+
+    def groups(*gs):
+        return (B.gpb_layer_group * len(gs))(*gs)
+
+    good = B.gpb_layer_group(a, ctypes.pointer(t.c), a, 10, a, 1152)
+    # groups, n, plan, S, NCP, T, PS
+    assert f(groups(good), 1, ctypes.byref(p), 0, 0, 0, 64, None, None) == B.OK
+    assert f(groups(good), 0, ctypes.byref(p), 4, 1, 5, 64, None, None) == B.EINVAL
+    assert f(groups(good), B.MAX_GROUPS + 1, ctypes.byref(p), 4, 1, 5, 64, None,
+             None) == B.EINVAL
+    assert f(groups(good), 1, None, 4, 1, 5, 64, None, None) == B.EINVAL
+    assert f(groups(good), 1, ctypes.byref(p), 4, 2, 1, 64, None, None) == B.EINVAL
+    big = B.Sources([(a, 10)] * (B.MAX_GROUP_SOURCES + 1))
+    over = B.gpb_layer_group(a, ctypes.pointer(big.c), a, 10, a, 1152)
+    assert f(groups(over), 1, ctypes.byref(p), 4, 1, 5, 64, None, None) == B.EINVAL
+    odd = B.gpb_layer_group(a, ctypes.pointer(t.c), a, 10, a, 1000)
+    assert f(groups(odd), 1, ctypes.byref(p), 4, 1, 5, 64, None, None) == B.EALIGN
+    mis = B.gpb_layer_group(a, ctypes.pointer(t.c), a + 8, 10, a, 1152)
+    assert f(groups(good, mis), 2, ctypes.byref(p), 4, 1, 5, 64, None, None) == B.EALIGN
+    nost = B.gpb_layer_group(a, ctypes.pointer(t.c), None, 10, a, 1152)
+    assert f(groups(nost), 1, ctypes.byref(p), 4, 1, 5, 64, None, None) == B.EINVAL
+    q = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+    q.d_prefix_desc = a + 4
+    assert f(groups(good), 1, ctypes.byref(q), 4, 1, 5, 64, None, None) == B.EALIGN
+
+
 def test_plan_build_clear_and_writer_counts_checks():
     m = _meta()
     fake = 0x100000

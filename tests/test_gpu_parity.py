@@ -746,9 +746,10 @@ def test_batch_replays_in_a_hip_graph(orc):
 
 @pytest.mark.parametrize("seed", range(2))
 def test_grouped_formats_match_single_format(orc, seed):
-    """One scatter launch and one gather launch for two to four row formats
-    (four, the most a launch takes, on the first batch) on one plan give, per
-    format, the single-format result (the oracle's)."""
+    """Two to four row formats (four, the most a launch takes, on the first
+    batch) on one plan, composed with one launch per layer for all of them
+    and with one scatter launch and one gather launch for all of them, give
+    per format the single-format result (the oracle's)."""
     gpb = _gpb()
     rng = np.random.default_rng(900 + seed)
     for i in range(12):
@@ -768,25 +769,27 @@ def test_grouped_formats_match_single_format(orc, seed):
             plan = r.plan
             runners.append(r)
             host.append((bk, pool_np, cur_np))
-        for r in runners:
-            r.begin_batch()
-            for d in r.dense:
-                d.fill_(POISON)
-        for layer in range(2):
-            gpb.layer_groups(runners, layer)
-        torch.cuda.synchronize()
-        want = _check_plan(host[0][0], runners[0], orc)
-        for r, (bk, pool_np, cur_np) in zip(runners, host):
+        for grouped in (gpb.layer_groups, gpb.layer_groups_two_launch):
+            for r in runners:
+                r.begin_batch()
+                for d in r.dense:
+                    d.fill_(POISON)
             for layer in range(2):
-                _check_layer(bk, r, layer, want, [pool_np], [cur_np], orc)
-            assert _status(r) == 0
+                grouped(runners, layer)
+            torch.cuda.synchronize()
+            want = _check_plan(host[0][0], runners[0], orc)
+            for r, (bk, pool_np, cur_np) in zip(runners, host):
+                for layer in range(2):
+                    _check_layer(bk, r, layer, want, [pool_np], [cur_np], orc)
+                assert _status(r) == 0
     _say("grouped seed", seed, "ok")
 
 
 def test_token_and_index_twin_in_one_launch_each(orc):
     """The traced batch's token KV (1152-byte rows) and index keys (144-byte
-    rows) composed with grouped launches, four layers with distinct arenas and
-    poisoned dense halves, byte-exact."""
+    rows) composed with grouped launches (one per layer, and scatter + gather),
+    four layers each with distinct arenas and poisoned dense halves,
+    byte-exact."""
     gpb = _gpb()
     b = workloads.make_batch("traced")
     rb = workloads.INDEX_ROW_BYTES
@@ -803,12 +806,13 @@ def test_token_and_index_twin_in_one_launch_each(orc):
     want = _check_plan(b, tok, orc)
     pools_np, curs_np = [_host(p) for p in pools], [_host(c) for c in curs]
     ipools_np, icurs_np = [_host(p) for p in ipools], [_host(c) for c in icurs]
-    for layer in range(4):
-        tok.dense[layer % 2].fill_(POISON)
-        twin.dense[layer % 2].fill_(POISON)
-        gpb.layer_groups([tok, twin], layer)
-        torch.cuda.synchronize()
-        _check_layer(b, tok, layer, want, pools_np, curs_np, orc)
-        _check_layer(bi, twin, layer, want, ipools_np, icurs_np, orc)
-        _say("  grouped layer", layer, "ok")
+    for grouped in (gpb.layer_groups, gpb.layer_groups_two_launch):
+        for layer in range(4):
+            tok.dense[layer % 2].fill_(POISON)
+            twin.dense[layer % 2].fill_(POISON)
+            grouped([tok, twin], layer)
+            torch.cuda.synchronize()
+            _check_layer(b, tok, layer, want, pools_np, curs_np, orc)
+            _check_layer(bi, twin, layer, want, ipools_np, icurs_np, orc)
+            _say("  grouped layer", layer, grouped.__name__, "ok")
     assert _status(tok) == 0 and _status(twin) == 0
