@@ -1,6 +1,7 @@
 """GPU tests at the size limits of the C ABI: byte offsets in 64 bits (a pool
-above 4 GiB read and filled past the 4 GiB mark), the 2 GiB buffer range of
-the staging region (rows written at its very end), and a 512 MiB page.  The
+above 4 GiB read and filled past the 4 GiB mark, by the gather and by the
+one-launch layer), the 2 GiB buffer range of the staging region (rows
+written at its very end), and 512 MiB pages.  The
 oracle's plain copies on host slices are the reference; only the slices the
 test touches are copied back."""
 import numpy as np
@@ -116,3 +117,75 @@ def test_fill_writes_pool_rows_beyond_4_gib(orc):
                         cur_np[np.r_[20:40, 0:20]], RB)
     assert np.array_equal(mid, sub[:30 * RB]) and np.array_equal(lo, sub[30 * RB:])
     assert np.array_equal(stag.cpu().numpy(), st)
+
+
+def _limits_runner(prefix_pages, cur_tokens, req_pages, n_pool_pages, PS, RB, seed):
+    """A one-rotation runner over a batch with the given page ids; the pool
+    is random bytes, the current rows too."""
+    import workloads
+    gpb = _gpb()
+    P = np.array(prefix_pages, np.int32)
+    c = np.array(cur_tokens, np.int32)
+    b = workloads.Batch("limits", len(P), PS, RB, n_pool_pages, 1, 1,
+                        workloads.staging_cap_for(int(c.sum()), len(P), PS), P, c,
+                        np.array(req_pages, np.int32))
+    pool = _rand(n_pool_pages * PS * RB, seed)
+    cur = _rand(int(c.sum()) * RB, seed + 1)
+    return gpb.ComposeRunner(gpb.BatchMeta.of(b), [pool], [cur]), pool, cur
+
+
+def _one_launch_equals_two(r):
+    """The one-launch layer against the two-launch layer (each checked
+    against the oracle elsewhere) on layers 0 and 1, dense poisoned first."""
+    r.begin_batch()
+    for layer in (0, 1):
+        r.dense[layer % 2].fill_(0xA5)
+        r.layer_two_launch(layer)
+        want = r.dense[layer % 2].clone()
+        r.dense[layer % 2].fill_(0x5A)
+        r.layer(layer)
+        torch.cuda.synchronize()
+        assert torch.equal(r.dense[layer % 2], want), "layer %d differs" % layer
+        del want
+    assert int(r.status.item()) == 0
+
+
+def test_one_launch_layer_reads_pages_beyond_4_gib(orc):
+    """Prefix pages past the 4 GiB mark of a 5 GiB pool, current pages at
+    its start, through the one-launch layer; the prefix rows also against
+    the pool's bytes."""
+    PS, RB = 64, 1152
+    page = PS * RB
+    n_pages = (5 * GIB) // page + 1
+    hi = n_pages - 1
+    # request 0: 3 prefix pages (all past 4 GiB), 2 current pages; request 1:
+    # 1 prefix page, 3 current pages
+    req = [hi, hi - 7, (4 * GIB) // page + 1, 5, 6, hi - 3, 9, 10, 11]
+    r, pool, cur = _limits_runner([3, 1], [100, 130], req, n_pages, PS, RB, 11)
+    _one_launch_equals_two(r)
+    dense = r.dense_of(1)
+    for slot, p in ((0, req[0]), (1, req[1]), (2, req[2]), (5, req[5])):
+        for row in (0, 17, PS - 1):
+            a = dense[slot * PS + row].cpu()
+            b = pool[p * page + row * RB:p * page + (row + 1) * RB].cpu()
+            assert torch.equal(a, b), (slot, row)
+    # current rows land at dense rows mixed_locs
+    ml = r.plan.t["mixed_locs"].cpu().numpy()
+    for t in (0, 99, 100, 229):
+        assert torch.equal(dense[int(ml[t])].cpu(), cur[t * RB:(t + 1) * RB].cpu())
+
+
+def test_one_launch_layer_half_gib_pages(orc):
+    """512 MiB pages through the one-launch layer: one prefix page, one
+    current page of 5,000 rows of 64 KiB, staging halves of 1.5 GiB."""
+    PS, RB = 8192, 65536
+    r, pool, cur = _limits_runner([1], [5000], [3, 1], 4, PS, RB, 21)
+    _one_launch_equals_two(r)
+    dense = r.dense_of(0)
+    page = PS * RB
+    for row in (0, 4095, PS - 1):
+        assert torch.equal(dense[row].cpu(), pool[3 * page + row * RB:3 * page + (row + 1) * RB].cpu())
+    for j in (0, 2500, 4999):
+        assert torch.equal(dense[PS + j].cpu(), cur[j * RB:(j + 1) * RB].cpu())
+    for j in (5000, PS - 1):
+        assert not dense[PS + j].any()
