@@ -744,6 +744,56 @@ def test_batch_replays_in_a_hip_graph(orc):
     assert _status(r) == 0
 
 
+@pytest.mark.parametrize("schedule", ["one_stream", "two_streams"])
+def test_layer_ahead_schedule_replays_in_a_hip_graph(orc, schedule):
+    """The layer-ahead schedules (one launch per layer on one stream; prefix
+    gathers on a second stream ordered by events) over four layers of the
+    medium batch with four arenas, captured once in a HIP graph: every
+    replay, with eager work that dirties every output in between, gives the
+    eager run's dense halves, staging and plan, and the last two layers match
+    the oracle."""
+    b = workloads.make_batch("medium")
+    L = 4
+    pools, curs = workloads.make_values(b, device="cuda", rotations=L)
+    r = _runner(b, pools, curs)
+    main = torch.cuda.current_stream()
+
+    def schedule_on(stream, side):
+        if schedule == "one_stream":
+            r.run_layer_ahead(L, stream)
+        else:
+            r.run_pipelined(L, stream, side, consume="fused")
+
+    schedule_on(main, torch.cuda.Stream())
+    torch.cuda.synchronize()
+    want = _check_plan(b, r, orc)
+    pools_np = [_host(p) for p in pools]
+    curs_np = [_host(c) for c in curs]
+    for layer in (L - 2, L - 1):
+        _check_layer(b, r, layer, want, pools_np, curs_np, orc)
+    ref = [t.clone() for t in r.dense + r.staging]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        schedule_on(cap, side)
+    for rep in range(3):
+        for k, t in enumerate(r.dense + r.staging):
+            t.fill_(0x11 * (k + 1))
+        for k in r.plan.t:
+            r.plan.t[k].fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b_ in zip(r.dense + r.staging, ref):
+            assert torch.equal(a, b_), "replay %d differs from the eager run" % rep
+        for k in oracle.PLAN_FIELDS:
+            assert np.array_equal(_host(r.plan.t[k]), want[k]), (rep, k)
+        _say("  replay", rep, schedule, "ok")
+    assert _status(r) == 0
+
+
 @pytest.mark.parametrize("seed", range(2))
 def test_grouped_formats_match_single_format(orc, seed):
     """Two to four row formats (four, the most a launch takes, on the first
