@@ -27,9 +27,10 @@
 
 #ifndef GPB_LAYER_STAGING_POLICY
 // cache-policy bits of the one-launch layer's staging stores and of its
-// read-back of those bytes: plain (write-back L2, cached loads), so the wave
-// that wrote a staging chunk reads it back from L2.  Interleaved probe on
-// MI355X, traced workload, us per layer (staging store / read-back):
+// read-back of those bytes: plain (write-back L2, cached loads), so a store
+// completes in L2 and the wave's read-back of the chunk does not wait on a
+// write through to memory.  Interleaved probe on MI355X, traced workload,
+// us per layer (staging store / read-back):
 //   sc1 / nt 96.0   plain / nt 89.4   plain / plain 87.4   sc0 / sc0 87.4
 //   sc0|sc1 / nt 96.0
 #define GPB_LAYER_STAGING_POLICY 0
