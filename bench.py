@@ -596,6 +596,7 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
     cur_ms = region(lambda: [runner.gather_current(l, stream) for l in range(L)], L) / L
     cons_ms = region(lambda: [runner.consume_fused(l, stream) for l in range(L)], L) / L
     fill_ms = region(lambda: [runner.fill(l, stream) for l in range(L)], L) / L
+    layer_fill_ms = region(lambda: [runner.layer_fill(l, stream) for l in range(L)], L) / L
     own = runner.writer_rows_of(0)
     W = len(runner.writer_counts)
     wsc_ms = region(lambda: [runner.scatter_writers(l, own, stream) for l in range(L)],
@@ -631,6 +632,7 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
         "consume_us": round((s_ms + cur_ms) * 1e3, 2),
         "consume_fused_us": round(cons_ms * 1e3, 2),
         "consume_with_fused_fill_us": round((fill_ms + cur_ms) * 1e3, 2),
+        "one_launch_layer_with_fused_fill_us": round(layer_fill_ms * 1e3, 2),
         "fused_fill_bytes": 3 * batch.n_cur_tokens * batch.row_bytes
                             + 8 * batch.n_cur_tokens,
         "pipelined_ms_per_step": round(pipe["fused"], 4),

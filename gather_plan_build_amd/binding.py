@@ -19,6 +19,7 @@ MAX_SOURCES = 64
 STATUS_BAD_DESCRIPTOR = 1
 STATUS_BAD_STAGING_ROW = 2
 STATUS_BAD_PLAN_INPUT = 4
+STATUS_LAYER_MISMATCH = 8
 
 OK, EINVAL, EALIGN, EPAGE, ECAPACITY, ERANGE, EHIP = 0, -1, -2, -3, -4, -5, -6
 
@@ -115,6 +116,9 @@ def _load(path):
                                       ctypes.POINTER(gpb_plan), i32, i32, vp, i64, vp, i32,
                                       i32, i32, vp, vp]
     lib.gpb_compose_consume.argtypes = lib.gpb_compose_layer.argtypes
+    lib.gpb_compose_layer_fill.argtypes = [vp, ctypes.POINTER(gpb_sources),
+                                           ctypes.POINTER(gpb_plan), i32, i32, vp, i64, vp,
+                                           i64, vp, i32, i32, i32, vp, vp]
     lib.gpb_compose_layer_ahead.argtypes = [vp] + list(lib.gpb_compose_layer.argtypes)
     lib.gpb_staging_clear.argtypes = [vp, i64, vp]
     lib.gpb_current_row_scatter.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp]
@@ -141,7 +145,8 @@ def _load(path):
 EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_plan_build_clear",
            "gpb_writer_counts", "gpb_staging_clear", "gpb_current_row_scatter",
            "gpb_compose_gather", "gpb_compose_gather_slots", "gpb_compose_gather_records",
-           "gpb_compose_layer", "gpb_compose_consume", "gpb_compose_layer_ahead",
+           "gpb_compose_layer", "gpb_compose_layer_fill", "gpb_compose_consume",
+           "gpb_compose_layer_ahead",
            "gpb_current_row_fill", "gpb_current_row_scatter_groups",
            "gpb_compose_gather_groups", "gpb_compose_layer_groups", "gpb_strerror")
 
@@ -397,6 +402,22 @@ def compose_layer(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging
                                  int(page_rows), int(row_bytes), _ptr(status),
                                  _stream(stream)),
            "gpb_compose_layer")
+
+
+def compose_layer_fill(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging_rows,
+                       pool, n_pool_rows, cur_rows, n_rows, page_rows, row_bytes, status=None,
+                       stream=None):
+    """The one-launch layer with the fused fill (current rows also to their
+    pool rows)."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_layer_fill(_ptr(dense), ctypes.byref(sources.c),
+                                      ctypes.byref(plan.c), int(n_slots), int(n_cur_pages),
+                                      _ptr(staging), int(n_staging_rows), _ptr(pool),
+                                      int(n_pool_rows), _ptr(cur_rows), int(n_rows),
+                                      int(page_rows), int(row_bytes), _ptr(status),
+                                      _stream(stream)),
+           "gpb_compose_layer_fill")
 
 
 def compose_consume(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging_rows,

@@ -108,20 +108,22 @@ __global__ __launch_bounds__(B) void k_compose_gather(
 // buffer for the prefix pages when the launch is layer l's consume together
 // with layer l + 1's prefetch (the table then lists layer l + 1's pool
 // entries and layer l's staging slabs).
-template <int B, bool SROWS>
+template <int B, bool SROWS, bool FILL>
 __global__ __launch_bounds__(B) void k_compose_layer(
     uint8_t *dense, uint8_t *dense_pre, SrcTable tbl, const int32_t *__restrict__ pre_desc,
     const int32_t *__restrict__ cur_desc, const int32_t *__restrict__ tok0,
     const int32_t *__restrict__ ntok, int32_t n_cur_units, uint8_t *staging,
     int32_t staging_bytes, int32_t n_staging_rows, const int32_t *__restrict__ rows,
     const uint8_t *__restrict__ cur, int32_t n_rows, int32_t row_chunks, int32_t n_slots,
-    int32_t page_bytes, int32_t parts, int32_t *status) {
+    int32_t page_bytes, int32_t parts, u32x4 *pool, int64_t n_pool_rows,
+    const int32_t *__restrict__ pool_locs, int32_t *status) {
   const bool is_cur = static_cast<int>(blockIdx.x) < n_cur_units;
   const int u = is_cur ? blockIdx.x : blockIdx.x - n_cur_units;
   const int k = u / parts;
-  layer_unit<B, SROWS>(tbl, dense, dense_pre, is_cur, k, u - k * parts, pre_desc, cur_desc,
-                       tok0, ntok, staging, staging_bytes, n_staging_rows, rows, cur, n_rows,
-                       row_chunks, n_slots, page_bytes, status);
+  layer_unit<B, SROWS, FILL>(tbl, dense, dense_pre, is_cur, k, u - k * parts, pre_desc,
+                             cur_desc, tok0, ntok, staging, staging_bytes, n_staging_rows,
+                             rows, cur, n_rows, row_chunks, n_slots, page_bytes, pool,
+                             n_pool_rows, pool_locs, status);
 }
 
 // Flat over (row, chunk) of the current rows: lane g of the grid handles
@@ -369,7 +371,9 @@ int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
                   const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
                   void *d_staging, int64_t n_staging_rows, const void *d_cur_rows,
                   int32_t n_rows, int32_t page_rows, int32_t row_bytes, int32_t *d_status,
-                  void *stream, bool with_prefix) {
+                  void *stream, bool with_prefix, void *d_pool = nullptr,
+                  int64_t n_pool_rows = -1) {
+  const bool fill = n_pool_rows >= 0;
   constexpr int B = 64;
   SrcTable t;
   int64_t page_bytes = 0;
@@ -389,11 +393,13 @@ int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
                           !plan->d_cur_page_ntok || !d_staging ||
                           (n_rows > 0 && (!plan->d_staging_rows || !d_cur_rows))))
     return GPB_EINVAL;
+  if (fill && n_cur_pages > 0 && (!d_pool || !plan->d_pool_locs)) return GPB_EINVAL;
   if (!aligned(d_dense, 16) || !aligned(plan->d_prefix_desc, 16) ||
       !aligned(plan->d_current_desc, 16) || !aligned(plan->d_cur_page_token0, 4) ||
       !aligned(plan->d_cur_page_ntok, 4) || !aligned(plan->d_staging_rows, 4) ||
       !aligned(d_staging, 16) || !aligned(d_cur_rows, 16))
     return GPB_EALIGN;
+  if (fill && (!aligned(d_pool, 16) || !aligned(plan->d_pool_locs, 4))) return GPB_EALIGN;
   const int64_t row_chunks = row_bytes / 16;
   const int64_t cur_bytes = static_cast<int64_t>(n_rows) * row_bytes;
   const int64_t staging_bytes = n_staging_rows * row_bytes;
@@ -404,14 +410,18 @@ int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
   if (grid == 0) return GPB_OK;
   // a unit of B chunks touches at most 2 + (B - 2) / row_chunks rows
   const bool srows = 2 + (B - 2) / row_chunks <= kScalarRows;
-  const auto kernel = srows ? k_compose_layer<B, true> : k_compose_layer<B, false>;
+  const auto kernel = fill ? (srows ? k_compose_layer<B, true, true>
+                                    : k_compose_layer<B, false, true>)
+                           : (srows ? k_compose_layer<B, true, false>
+                                    : k_compose_layer<B, false, false>);
   return launch(kernel, dim3(static_cast<uint32_t>(grid)), dim3(B), as_stream(stream),
                 d_dense, with_prefix ? d_dense_pre : d_dense, t, plan->d_prefix_desc,
                 plan->d_current_desc,
                 plan->d_cur_page_token0, plan->d_cur_page_ntok,
                 static_cast<int32_t>(parts * n_cur_pages), d_staging, staging_bytes,
                 n_staging_rows, plan->d_staging_rows, d_cur_rows, n_rows,
-                static_cast<int32_t>(row_chunks), n_slots, page_bytes, parts, d_status);
+                static_cast<int32_t>(row_chunks), n_slots, page_bytes, parts, d_pool,
+                fill ? n_pool_rows : 0, fill ? plan->d_pool_locs : nullptr, d_status);
 }
 }  // namespace
 }  // namespace gpb
@@ -424,6 +434,19 @@ extern "C" int gpb_compose_layer(void *d_dense, const gpb_sources *table,
   return gpb::compose_layer(d_dense, d_dense, table, plan, n_slots, n_cur_pages, d_staging,
                             n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
                             d_status, stream, true);
+}
+
+extern "C" int gpb_compose_layer_fill(void *d_dense, const gpb_sources *table,
+                                      const gpb_plan *plan, int32_t n_slots,
+                                      int32_t n_cur_pages, void *d_staging,
+                                      int64_t n_staging_rows, void *d_pool,
+                                      int64_t n_pool_rows, const void *d_cur_rows,
+                                      int32_t n_rows, int32_t page_rows, int32_t row_bytes,
+                                      int32_t *d_status, void *stream) {
+  if (n_pool_rows < 0) return GPB_EINVAL;
+  return gpb::compose_layer(d_dense, d_dense, table, plan, n_slots, n_cur_pages, d_staging,
+                            n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
+                            d_status, stream, true, d_pool, n_pool_rows);
 }
 
 extern "C" int gpb_compose_layer_ahead(void *d_dense, void *d_dense_next,

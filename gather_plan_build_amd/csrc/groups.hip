@@ -130,15 +130,17 @@ __global__ __launch_bounds__(kUnitLanes) void k_layer_groups(
   const int u = unit - (is_cur ? gr.cur_begin : gr.pre_begin);
   const int k = u / gr.parts;
   if (gr.srows)
-    layer_unit<kUnitLanes, true>(gr.tbl, gr.dense, gr.dense, is_cur, k, u - k * gr.parts,
-                                 pre_desc, cur_desc, tok0, ntok, gr.staging, gr.staging_bytes,
-                                 gr.n_staging_rows, rows, gr.cur, n_rows, gr.row_chunks,
-                                 n_slots, gr.page_bytes, status);
+    layer_unit<kUnitLanes, true, false>(gr.tbl, gr.dense, gr.dense, is_cur, k,
+                                        u - k * gr.parts, pre_desc, cur_desc, tok0, ntok,
+                                        gr.staging, gr.staging_bytes, gr.n_staging_rows, rows,
+                                        gr.cur, n_rows, gr.row_chunks, n_slots, gr.page_bytes,
+                                        nullptr, 0, nullptr, status);
   else
-    layer_unit<kUnitLanes, false>(gr.tbl, gr.dense, gr.dense, is_cur, k, u - k * gr.parts,
-                                  pre_desc, cur_desc, tok0, ntok, gr.staging, gr.staging_bytes,
-                                  gr.n_staging_rows, rows, gr.cur, n_rows, gr.row_chunks,
-                                  n_slots, gr.page_bytes, status);
+    layer_unit<kUnitLanes, false, false>(gr.tbl, gr.dense, gr.dense, is_cur, k,
+                                         u - k * gr.parts, pre_desc, cur_desc, tok0, ntok,
+                                         gr.staging, gr.staging_bytes, gr.n_staging_rows, rows,
+                                         gr.cur, n_rows, gr.row_chunks, n_slots, gr.page_bytes,
+                                         nullptr, 0, nullptr, status);
 }
 
 }  // namespace

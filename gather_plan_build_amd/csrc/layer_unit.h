@@ -39,20 +39,28 @@ struct ArenaTable {
 // the plain cache policy: the store completes in L2 instead of writing
 // through to memory, so the read-back does not wait on a trip to memory
 // (part of it is served by L2 itself).  The two-launch path's scatter
-// writes through instead, since its reader is another kernel.
+// writes through instead, since its reader is another kernel.  A lane that
+// wrote a current row's chunk also checks that its read-back addressed that
+// chunk (GPB_STATUS_LAYER_MISMATCH otherwise: a table or plan that breaks
+// the layout); the unit's status bits are ORed in once, after its stores.
 //
 // A prefix unit copies its KiB of a pool page into dense_pre; a current unit
 // stores into dense.  With SROWS (rows of at least 21 chunks) a unit spans
 // at most kScalarRows rows, whose staging rows are fetched once with scalar
-// loads.
-template <int B, bool SROWS, typename Table>
+// loads.  With FILL a current unit also writes each current-row chunk to the
+// token's pool row pool_locs[t] (the fused fill: the KV-cache store and the
+// staging fill in one pass), with a 64-bit address since a pool may exceed
+// one buffer range; the pool rows of current tokens are never pages the
+// gather reads.
+template <int B, bool SROWS, bool FILL, typename Table>
 __device__ __forceinline__ void layer_unit(
     const Table &tbl, uint8_t *dense, uint8_t *dense_pre, bool is_cur, int k, int part,
     const int32_t *__restrict__ pre_desc, const int32_t *__restrict__ cur_desc,
     const int32_t *__restrict__ tok0, const int32_t *__restrict__ ntok, uint8_t *staging,
     int32_t staging_bytes, int32_t n_staging_rows, const int32_t *__restrict__ rows,
     const uint8_t *__restrict__ cur, int32_t n_rows, int32_t row_chunks, int32_t n_slots,
-    int32_t page_bytes, int32_t *status) {
+    int32_t page_bytes, u32x4 *pool, int64_t n_pool_rows,
+    const int32_t *__restrict__ pool_locs, int32_t *status) {
   const i32x4 rec = reinterpret_cast<const i32x4 *>(is_cur ? cur_desc : pre_desc)[k];
   const int slot = rec.x, e = rec.y, p = rec.z;
   if (slot < 0 || slot >= n_slots) {
@@ -61,6 +69,8 @@ __device__ __forceinline__ void layer_unit(
   }
   const int c = part * B + threadIdx.x;  // 16-byte chunk of the page
   const uint32_t off = static_cast<uint32_t>(c) * 16u;
+  int flags = 0;
+  const uint8_t *wrote = nullptr;  // staging byte this lane wrote (current rows)
   if (is_cur) {
     const int t0 = tok0[k], nt = ntok[k];
     const int j = c / row_chunks;  // row of the page
@@ -84,10 +94,19 @@ __device__ __forceinline__ void layer_unit(
     const bool ok = in_rows && d >= 0 && d < n_staging_rows;
     const __amdgpu_buffer_rsrc_t rc = rsrc(cur, n_rows * row_chunks * 16);
     const __amdgpu_buffer_rsrc_t rst = rsrc(staging, staging_bytes);
+    const uint32_t to = static_cast<uint32_t>(d * row_chunks + oc) * 16u;
     const u32x4 v = ld16(rc, in_rows ? static_cast<uint32_t>(t * row_chunks + oc) * 16u
                                      : kDropOffset);
-    st16_staged(v, rst, ok ? static_cast<uint32_t>(d * row_chunks + oc) * 16u : kDropOffset);
-    if (live && !ok && status) atomicOr(status, GPB_STATUS_BAD_STAGING_ROW);
+    st16_staged(v, rst, ok ? to : kDropOffset);
+    bool bad = live && !ok;
+    if (FILL) {
+      const int64_t q = pool_locs[in_rows ? t : 0];
+      const bool okp = in_rows && q >= 0 && q < n_pool_rows;
+      bad |= in_rows && !okp;
+      if (okp) __builtin_nontemporal_store(v, pool + q * row_chunks + oc);
+    }
+    if (bad) flags |= GPB_STATUS_BAD_STAGING_ROW;
+    if (ok) wrote = staging + to;
   }
   const bool sentinel = (e < 0) || (p < 0);
   const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
@@ -98,8 +117,10 @@ __device__ __forceinline__ void layer_unit(
   // a current page's bytes were just written by this very wave: read them
   // back through the cache; pool pages are streamed
   st16_dense(is_cur ? ld16_staged(rs, off) : ld16(rs, off), rd, off);
-  if (!sentinel && !in_table && status && part == 0 && threadIdx.x == 0)
-    atomicOr(status, GPB_STATUS_BAD_DESCRIPTOR);
+  if (wrote && in_table && from + off != wrote) flags |= GPB_STATUS_LAYER_MISMATCH;
+  if (!sentinel && !in_table && part == 0 && threadIdx.x == 0)
+    flags |= GPB_STATUS_BAD_DESCRIPTOR;
+  if (flags && status) atomicOr(status, flags);
 }
 
 }  // namespace gpb

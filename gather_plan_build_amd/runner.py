@@ -149,6 +149,16 @@ class ComposeRunner:
                         self.curs[layer % len(self.curs)], self.T, self.ps, self.rb,
                         self.status, stream)
 
+    def layer_fill(self, layer, stream=None):
+        """The one-launch layer with the fused fill: the current rows also go
+        to their pool rows in the layer's pool arena."""
+        h, k = layer % PARITY, layer % len(self.pools)
+        pool = self.pools[k]
+        B.compose_layer_fill(self.dense[h], self.tables[(k, h)], self.plan, self.S,
+                             self.plan.NCP, self.staging[h], self.staging_rows_total, pool,
+                             self.n_pool_pages * self.ps, self.curs[layer % len(self.curs)],
+                             self.T, self.ps, self.rb, self.status, stream)
+
     def consume_fused(self, layer, stream=None):
         """The consume half in one launch: the scatter and the gather of the
         current pages."""

@@ -109,6 +109,13 @@ typedef enum gpb_status {
                                         the validated host copy (a page id or
                                         index out of range); the entry is not
                                         written                              */
+#define GPB_STATUS_LAYER_MISMATCH 8  /* one-launch layer: a current row's
+                                        staging row is not where its page's
+                                        descriptor reads the page back (a
+                                        table whose staging entries are not
+                                        the slabs of d_staging, or a plan of
+                                        another batch); that page's dense
+                                        bytes are not reliable               */
 
 #define GPB_MAX_SOURCES 64           /* pointer-table entries per gather    */
 
@@ -365,7 +372,10 @@ int gpb_compose_gather_records(void *d_dense, const gpb_sources *table,
  * staging rows address (the layout gpb_plan_build assumes: slab w at
  * d_staging + w * CAP * page_rows * row_bytes), and the staging rows a batch
  * does not write must hold zeros (gpb_staging_clear or gpb_plan_build_clear
- * once per batch).  Rows must not repeat (the plan's do not).  Errors as the
+ * once per batch).  Rows must not repeat (the plan's do not).  Every lane
+ * that writes a current row's chunk checks that its read-back addresses
+ * that same chunk; when the table or plan breaks the layout it ORs
+ * GPB_STATUS_LAYER_MISMATCH into *d_status (if not NULL).  Errors as the
  * two calls, plus GPB_EINVAL for plan NULL or n_cur_pages outside
  * [0, min(n_slots, n_rows)]. */
 int gpb_compose_layer(void *d_dense, const gpb_sources *table, const gpb_plan *plan,
@@ -373,6 +383,22 @@ int gpb_compose_layer(void *d_dense, const gpb_sources *table, const gpb_plan *p
                       int64_t n_staging_rows, const void *d_cur_rows, int32_t n_rows,
                       int32_t page_rows, int32_t row_bytes, int32_t *d_status,
                       void *stream);
+
+/* Per layer, gpb_compose_layer with the fused current fill (the fill of
+ * gpb_current_row_fill: each current row also goes to its pool row
+ * plan->d_pool_locs[t] of d_pool, a pool of n_pool_rows rows, whatever its
+ * size): the KV-cache store of the current rows, their staging fill and the
+ * whole gather in one launch.  The pool rows written are the current
+ * tokens' own, never pages the gather reads.  A pool row outside
+ * [0, n_pool_rows) is skipped there and GPB_STATUS_BAD_STAGING_ROW is ORed
+ * into *d_status.  Errors as gpb_compose_layer, plus GPB_EINVAL for
+ * n_pool_rows < 0 or a NULL pool or pool_locs with current pages, and
+ * GPB_EALIGN for a pool not 16-byte aligned. */
+int gpb_compose_layer_fill(void *d_dense, const gpb_sources *table, const gpb_plan *plan,
+                           int32_t n_slots, int32_t n_cur_pages, void *d_staging,
+                           int64_t n_staging_rows, void *d_pool, int64_t n_pool_rows,
+                           const void *d_cur_rows, int32_t n_rows, int32_t page_rows,
+                           int32_t row_bytes, int32_t *d_status, void *stream);
 
 /* Per layer, the consume half of the layer-ahead split in one launch (page
  * 0d87bc5, commit "prefetch staging exchange": the consume step fills the

@@ -139,6 +139,27 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
     }
   }
 
+  /* the one-launch layer with the fused fill into a copy of the pool: same
+   * dense and staging; the pool is checked with the separate fill below */
+  {
+    gpb_sources t3 = *t;
+    for (int w = 0; w < b->n_writers; w++)
+      t3.base[b->n_pool_entries + w] =
+          (uint8_t *)d_stag2 + (size_t)w * b->staging_cap_pages * PS * RB;
+    HCHECK(hipMemcpy(d_pool2, d_pool, pool_bytes, hipMemcpyDeviceToDevice));
+    CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
+    HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
+    CHECK(gpb_compose_layer_fill(d_dense2, &t3, p, S, NCP, d_stag2, (int64_t)stag_rows,
+                                 d_pool2, (int64_t)(b->n_pool_pages * PS), d_cur, T,
+                                 b->page_size, b->row_bytes, d_status, st));
+    HCHECK(hipStreamSynchronize(st));
+    if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB) ||
+        !same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+      fprintf(stderr, "one-launch layer with fill differs from the two-call layer\n");
+      return 14;
+    }
+  }
+
   /* fused fill into a copy of the pool */
   HCHECK(hipMemcpy(d_pool2, d_pool, pool_bytes, hipMemcpyDeviceToDevice));
   CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
@@ -283,7 +304,7 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
   HCHECK(hipFree(d_stag2));
   HCHECK(hipFree(d_pool2));
   printf("c consumer: slot-list and record gathers, grouped calls, fused fill, one-launch "
-         "layer (single and grouped), fused consume, layer ahead, per-writer scatters and "
+         "layer (single, grouped, with fill), fused consume, layer ahead, per-writer scatters and "
          "plan build with clear agree\n");
   return 0;
 }

@@ -240,6 +240,26 @@ def test_layer_groups_argument_checks():
     assert f(groups(good), 1, ctypes.byref(q), 4, 1, 5, 64, None, None) == B.EALIGN
 
 
+def test_layer_fill_argument_checks():
+    f = B.lib.gpb_compose_layer_fill
+    a = 0x100000
+    t = B.Sources([(a, 10), (a, 4)])
+    p = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+    # dense, table, plan, S, NCP, staging, staging rows, pool, pool rows, cur, T, PS, RB
+    assert f(a, ctypes.byref(t.c), ctypes.byref(p), 0, 0, a, 10, a, 100, a, 0, 64, 1152,
+             None, None) == B.OK
+    assert f(a, ctypes.byref(t.c), ctypes.byref(p), 4, 1, a, 10, a, -1, a, 5, 64, 1152,
+             None, None) == B.EINVAL
+    assert f(a, ctypes.byref(t.c), ctypes.byref(p), 4, 1, a, 10, None, 100, a, 5, 64, 1152,
+             None, None) == B.EINVAL
+    assert f(a, ctypes.byref(t.c), ctypes.byref(p), 4, 1, a, 10, a + 8, 100, a, 5, 64, 1152,
+             None, None) == B.EALIGN
+    q = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+    q.d_pool_locs = None
+    assert f(a, ctypes.byref(t.c), ctypes.byref(q), 4, 1, a, 10, a, 100, a, 5, 64, 1152,
+             None, None) == B.EINVAL
+
+
 def test_plan_build_clear_and_writer_counts_checks():
     m = _meta()
     fake = 0x100000

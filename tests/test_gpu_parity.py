@@ -196,6 +196,9 @@ def test_multi_layer_workloads(orc, name):
         _check_one_launch(b, r, layer, want, pools_np[layer % len(pools_np)],
                           curs_np[layer % len(curs_np)], orc)
         _say("  one-launch layer and fused consume", layer, "ok")
+    _check_layer_fill(b, r, 1, want, pools_np[1 % len(pools_np)], curs_np[1 % len(curs_np)],
+                      orc)
+    _say("  one-launch layer with fused fill ok")
     assert _status(r) == 0
 
 
@@ -259,6 +262,29 @@ def _check_one_launch(batch, r, layer, want_plan, pool_np, cur_np, orc):
     assert np.array_equal(_host(r.staging_of(layer)), staging), "fused consume staging differs"
 
 
+def _check_layer_fill(batch, r, layer, want_plan, pool_np, cur_np, orc):
+    """The one-launch layer with the fused fill: dense and staging equal the
+    oracle's layer; the pool holds each current row at its pool row and no
+    other pool byte changed (the oracle's fill); the pool is restored
+    afterwards."""
+    dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
+    pool_after = pool_np.reshape(-1, batch.row_bytes).copy()
+    st = np.zeros(batch.staging_rows_total * batch.row_bytes, np.uint8)
+    assert not orc.fill(st, want_plan["staging_rows"], pool_after.reshape(-1),
+                        want_plan["pool_locs"], cur_np, batch.row_bytes)
+    h, k = layer % 2, layer % len(r.pools)
+    r.staging[h].zero_()
+    r.dense[h].fill_(POISON)
+    r.layer_fill(layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(r.dense_of(layer)), dense), "layer with fill: dense differs"
+    assert np.array_equal(_host(r.staging_of(layer)), staging), \
+        "layer with fill: staging differs"
+    assert np.array_equal(_host(r.pools[k]).reshape(-1, batch.row_bytes), pool_after), \
+        "layer with fill: pool differs"
+    r.pools[k].copy_(torch.from_numpy(pool_np.reshape(r.pools[k].shape)))
+
+
 def _check_writer_scatters(batch, r, layer, want_plan, pool_np, cur_np, orc):
     """The scatter run as W writers, each copying its own rows (in its list
     order) into its own slab, then one gather: staging and dense equal the
@@ -291,6 +317,7 @@ def _random_case(orc, b, layers=2):
     _check_split(b, r, layers + 1, want, pool_np, cur_np, orc, fused_fill=True)
     _check_one_launch(b, r, layers, want, pool_np, cur_np, orc)
     _check_writer_scatters(b, r, layers + 1, want, pool_np, cur_np, orc)
+    _check_layer_fill(b, r, layers, want, pool_np, cur_np, orc)
     assert _status(r) == 0
 
 
@@ -383,6 +410,31 @@ def test_shared_plan_must_match_the_batch(orc):
                         b.req_pages)
     with pytest.raises(ValueError):
         gpb.ComposeRunner(bad, ipools, icurs, plan=tok.plan)
+
+
+def test_one_launch_layer_reports_a_table_that_breaks_the_layout(orc):
+    """The one-launch layer reads each current page back through the table;
+    a table whose staging entry is not the staging the rows are written to
+    is reported (GPB_STATUS_LAYER_MISMATCH), while the same call with the
+    plan's layout reports nothing."""
+    gpb = _gpb()
+    b = workloads.make_batch("tiny")
+    pools, curs = workloads.make_values(b, device="cuda")
+    r = _runner(b, pools, curs)
+    r.begin_batch()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    good = r.tables[(0, 0)]
+    gpb.compose_layer(r.dense[0], good, r.plan, r.S, r.plan.NCP, r.staging[0],
+                      r.staging_rows_total, curs[0], r.T, r.ps, r.rb, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    elsewhere = torch.zeros_like(r.staging[0])
+    bad = gpb.Sources([(pools[0], b.n_pool_pages)] * b.n_pool_entries +
+                      [(elsewhere, b.staging_cap_pages)] * b.n_writers)
+    gpb.compose_layer(r.dense[0], bad, r.plan, r.S, r.plan.NCP, r.staging[0],
+                      r.staging_rows_total, curs[0], r.T, r.ps, r.rb, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == gpb.STATUS_LAYER_MISMATCH
 
 
 def test_records_out_of_range_are_skipped(orc):
