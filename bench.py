@@ -71,11 +71,21 @@ DIGEST_FILES = ("gather_plan_build_amd/csrc/compose.hip",
                 "gather_plan_build_amd/csrc/gpb_common.h")
 
 
+def _code_of(text):
+    """C/C++ source without comments and with whitespace collapsed, so that
+    a comment edit does not count as a change of the code the counters were
+    taken on."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def _source_digest():
     h = hashlib.sha256()
     for name in DIGEST_FILES:
-        with open(os.path.join(ROOT, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(ROOT, name)) as f:
+            h.update(name.encode() + _code_of(f.read()).encode())
     return h.hexdigest()[:16]
 
 

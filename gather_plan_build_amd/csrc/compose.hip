@@ -10,18 +10,25 @@
 // "compose_v2": an owner or src of -1 yields a zero page.  Page 0d87bc5,
 // commit "fp8 index_copy_ -> uint8 views": rows are raw bytes.
 //
-// Both per-layer kernels are HBM-bound copies with no arithmetic to speak of,
-// so the design is about the memory system only:
+// Kernels: k_compose_layer, both steps of a layer in one launch (the
+// default; its unit is in layer_unit.h), and k_row_scatter and
+// k_compose_gather, the two steps apart (for callers whose scatter and
+// gather sit on two sides of a barrier, as on several GPUs).  All are
+// HBM-bound copies with no arithmetic to speak of, so the design is about
+// the memory system only:
 //   - every lane moves 16-byte chunks (buffer_load_dwordx4 /
 //     buffer_store_dwordx4), a wave64 moves one contiguous KiB per
 //     instruction;
 //   - the work is cut into many small units (one wave, one KiB per unit by
 //     default), walked in address order: on MI355X this measured faster than
 //     fewer, larger units (more chunks in flight per lane, 256-lane
-//     workgroups), than part-major orders and than XCD-blocked orders;
-//   - loads are non-temporal (each byte is read once per layer); the dense
-//     stores carry nt|sc1 and the staging stores sc1, each measured fastest
-//     for its kernel here;
+//     workgroups), than part-major orders, than XCD-blocked orders and than a
+//     persistent grid looping over the units;
+//   - pool and current-row loads are non-temporal (each byte is read once
+//     per layer); the dense stores carry nt|sc1; the separate scatter's
+//     staging stores carry sc1 (their reader is the next kernel), the
+//     one-launch layer's staging stores and read-back the plain policy (the
+//     reader is the same wave), each measured fastest for its kernel here;
 //   - raw buffer resources bound every access, so ragged tails, -1 sentinels
 //     and bad rows cost no branches.
 // The unit shape and cache-policy bits can be overridden at build time
