@@ -555,6 +555,8 @@ def main():
     # launch moves the layer's algorithmic bytes
     achieved = layer_bytes / (layer_ms * 1e-3) / 1e9
     out["us_per_layer"] = round(layer_ms * 1e3, 2)
+    # the same figure from the headline region: (step - plan and clear) / L
+    out["us_per_layer_from_step"] = round((ms_per_step - p_ms) * 1e3 / L, 2)
     out["pct_of_peak"] = round(100.0 * achieved / HBM_PEAK_GBS, 2)
     out["kernels_us"] = {"compose_layer": round(layer_ms * 1e3, 2),
                          "compose_gather": round(g_us, 2),
