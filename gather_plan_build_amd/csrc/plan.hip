@@ -2,10 +2,10 @@
 //
 // Page d63fbd4, commit "current rows written straight into staging": the
 // plan carries a staging-remapped page inverse that retargets the fill, and
-// the layer-invariant mixed_locs / staging row indices are built once per
-// batch.  Page d63fbd4, commit "cut per-layer CPU on the prefill launch
-// path": the ragged int32 descriptors and slot spans come from batch
-// metadata only, with no device synchronisation.  Page 0d87bc5, commit
+// mixed_locs and the staging row indices, which no layer changes, come from
+// one pass per batch.  Page d63fbd4, commit "cut per-layer CPU on the
+// prefill launch path": the ragged int32 descriptors and slot spans come
+// from batch metadata only, with no device synchronisation.  Page 0d87bc5, commit
 // "prefetch staging exchange": page 0 is the dummy page and the staging slot
 // of current page i is i + 1.
 //

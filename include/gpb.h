@@ -6,7 +6,7 @@
  * descriptors (owner, src), per-token staging rows and mixed_locs, and the
  * ragged int32 descriptors (gpb_plan_build_clear also zeroes the staging
  * region in the same launches).  Per layer, gpb_current_row_scatter writes
- * the current token rows into the zeroed staging span and gpb_compose_gather
+ * the current token rows into staging cleared once per batch, gpb_compose_gather
  * fills the slot-dense KV buffer one page per slot from a pointer table of
  * source arenas [pool entries || staging slabs]; gpb_compose_layer does both
  * in one launch.  The layer-ahead split gathers a layer's prefix pages
@@ -173,8 +173,8 @@ typedef struct gpb_batch {
  * Per-token ragged expansions (page d63fbd4, commit "cut per-layer CPU on the
  * prefill launch path": the O(total-q-tokens) top-k offset list and segment
  * records of the ragged index plan; page 0d87bc5, commit "flattened request
- * row ids": row ids built once per batch instead of a per-layer
- * repeat_interleave):
+ * row ids": the row ids come from the plan, computed a single time for the
+ * batch, where a repeat_interleave per layer made them before):
  *   token_req[t]          request of current token t (flattened row id)  [T]
  *   topk_offsets[t]       k_bases of that request: a request-relative KV
  *                         position plus this offset is a dense row       [T]
@@ -277,8 +277,8 @@ int gpb_writer_counts(const gpb_batch *batch, int32_t *h_counts);
 /* Zero `n_bytes` bytes at d_ptr (n_bytes a multiple of 16, d_ptr 16-byte
  * aligned): the per-batch clear of the staging region, so the rows of a last
  * current page past its request's tokens read back as zero (page d63fbd4,
- * commit "current rows written straight into staging": the fill writes into
- * the zeroed staging span).  The staging rows a batch writes are the same in
+ * commit "current rows written straight into staging": the rows land in
+ * staging that holds zeros wherever no row is written).  The staging rows a batch writes are the same in
  * every layer, so one clear per batch serves all its layers.  A kernel, not a
  * memset node, so the call can be captured in a HIP graph.  Errors:
  * GPB_EINVAL (n_bytes < 0, or d_ptr NULL with n_bytes > 0), GPB_EALIGN,
@@ -292,7 +292,7 @@ int gpb_staging_clear(void *d_ptr, int64_t n_bytes, void *stream);
  * contiguous rows; d_staging holds n_staging_rows rows.  A staging row
  * outside [0, n_staging_rows) is skipped and GPB_STATUS_BAD_STAGING_ROW is
  * ORed into *d_status when d_status is not NULL (page 0d87bc5: index_copy_
- * has no skip semantics for a stray -1, so the plan must never emit one).
+ * cannot leave out an index of -1, so a valid plan holds none).
  * Rows must not repeat (the plan's rows are distinct), and the staging region
  * must not overlap the current rows.  Errors: GPB_EINVAL (negative sizes,
  * row_bytes < 1, a NULL pointer with n_rows > 0), GPB_EALIGN, GPB_ERANGE (the

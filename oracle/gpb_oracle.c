@@ -206,8 +206,8 @@ int gpbo_plan(int32_t bs, int32_t page_size, int32_t row_bytes,
   }
 
   /* O9: per current token, its pool location (loc) and the staging row the
-   * fill writes, found through the staging-remapped page inverse exactly as
-   * the fill kernels take their destinations from a page inverse [SD];
+   * fill writes, found through the staging-remapped page inverse, the same
+   * route by which the pages' fill reaches its destinations [SD];
    * mixed_locs is the token's row in the dense buffer. */
   for (int32_t r = 0; r < bs; r++) {
     for (int32_t j = 0; j < cur_tokens[r]; j++) {
@@ -262,7 +262,7 @@ int gpbo_layer(const uint8_t *const *table, const int64_t *table_pages,
 }
 
 /*
- * O12: per-token ragged expansions, built once per batch ([CG]: the
+ * O12: per-token ragged expansions, one set per batch ([CG]: the
  * O(total-q-tokens) top-k offset list and the segment records of the ragged
  * index plan; page 0d87bc5, commit "flattened request row ids": row ids that
  * the pages built with repeat_interleave over per-request lengths).  For every
