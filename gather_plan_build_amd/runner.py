@@ -243,16 +243,6 @@ class ComposeRunner:
                            self.n_pool_pages * self.ps, self.plan.t["pool_locs"],
                            self.curs[k], self.T, self.rb, self.status, stream)
 
-    def layer_split(self, layer, stream=None, fused_fill=False):
-        """One layer as prefetch (prefix gather) then consume (fill or
-        scatter, then the current-page gather)."""
-        self.gather_prefix(layer, stream)
-        if fused_fill:
-            self.fill(layer, stream)
-        else:
-            self.scatter(layer, stream)
-        self.gather_current(layer, stream)
-
     def run(self, n_layers, stream=None):
         self.begin_batch(stream)
         for l in range(n_layers):
@@ -336,9 +326,6 @@ class ComposeRunner:
 
     def gather_bytes(self):
         return 2 * self.S * self.ps * self.rb + 8 * self.S
-
-    def scatter_bytes(self):
-        return 2 * self.T * self.rb + 4 * self.T
 
 
 def layer_groups(runners, layer, stream=None):
