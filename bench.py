@@ -577,6 +577,7 @@ def main():
         a.twin_index_bytes = 0
     else:
         _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead)
+        out["ceilings"] = _ceilings(gpb, stream, lead, achieved)
     assert int(runner.status.item()) == 0
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib << 20
@@ -588,6 +589,27 @@ def main():
     if a.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(batch, pools, curs, a.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _ceilings(gpb, stream, lead, achieved_gbs):
+    """What plain streams reach on this GPU, as context for the roofline
+    fraction: a write-only fill (the library's staging clear) and a torch
+    device copy (read + write), each over 1 GiB buffers, four times what the
+    256 MB MALL holds, in GPU-only regions."""
+    import torch
+    n, reps = 1 << 30, 10
+    x = torch.ones(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    fill_ms = _timed(stream, lambda: gpb.staging_clear(y, stream=stream), reps,
+                     lead=lead(reps))
+    copy_ms = _timed(stream, lambda: y.copy_(x), reps, lead=lead(reps))
+    del x, y
+    torch.cuda.empty_cache()
+    fill_gbs = n / (fill_ms * 1e-3) / 1e9
+    return {"buffer_bytes": n,
+            "fill_write_gbs": round(fill_gbs, 1),
+            "torch_copy_read_write_gbs": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "compose_layer_over_fill": round(achieved_gbs / fill_gbs, 4)}
 
 
 def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
