@@ -262,6 +262,33 @@ def _check_one_launch(batch, r, layer, want_plan, pool_np, cur_np, orc):
     assert np.array_equal(_host(r.staging_of(layer)), staging), "fused consume staging differs"
 
 
+def _check_layer_ahead(batch, r, layer, want_plan, pool_np, cur_np, orc):
+    """The layer-ahead launch (gpb_compose_layer_ahead) on one batch whose
+    layers share one pool and one set of current rows: after layer l's
+    prefix gather, one launch consumes layer l into its half and gathers
+    layer l + 1's prefix pages into the other half.  Layer l's half and its
+    staging equal the oracle's layer; the other half holds the oracle's
+    prefix pages, and its current slots keep their poison."""
+    assert len(r.pools) == 1 and len(r.curs) == 1
+    dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
+    h = layer % 2
+    r.staging[h].zero_()
+    r.dense[h].fill_(POISON)
+    r.dense[1 - h].fill_(POISON)
+    r.gather_prefix(layer)
+    r.ahead(layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(r.dense_of(layer)), dense), "layer-ahead: consumed half differs"
+    assert np.array_equal(_host(r.staging_of(layer)), staging), "layer-ahead: staging differs"
+    nxt = _host(r.dense_of(layer + 1))
+    PS = batch.page_size
+    cur = np.zeros(len(nxt) // PS if PS else 0, bool)
+    cur[want_plan["current_slots"]] = True
+    rows_cur = np.repeat(cur, PS)
+    assert np.array_equal(nxt[~rows_cur], dense[~rows_cur]), "layer-ahead: prefix pages differ"
+    assert (nxt[rows_cur] == POISON).all(), "layer-ahead: wrote a current slot of the next half"
+
+
 def _check_layer_fill(batch, r, layer, want_plan, pool_np, cur_np, orc):
     """The one-launch layer with the fused fill: dense and staging equal the
     oracle's layer; the pool holds each current row at its pool row and no
@@ -318,6 +345,7 @@ def _random_case(orc, b, layers=2):
     _check_one_launch(b, r, layers, want, pool_np, cur_np, orc)
     _check_writer_scatters(b, r, layers + 1, want, pool_np, cur_np, orc)
     _check_layer_fill(b, r, layers, want, pool_np, cur_np, orc)
+    _check_layer_ahead(b, r, layers + 1, want, pool_np, cur_np, orc)
     assert _status(r) == 0
 
 
