@@ -29,6 +29,9 @@ def command(out, defines=()):
            "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Werror",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # the leading kernel arguments arrive in scalar registers at wave
+           # launch instead of being read from the argument segment
+           "-mllvm", "-amdgpu-kernarg-preload-count=16",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
     cmd += ["-D" + d for d in defines]
     return cmd + ["-o", out] + sources()

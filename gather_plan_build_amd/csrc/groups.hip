@@ -23,9 +23,8 @@ constexpr int kUnitLanes = 64;  // one wave64 per unit, one 16-byte chunk per la
 
 struct GatherGroupArgs {
   uint8_t *dense;
-  const uint8_t *base[GPB_MAX_GROUP_SOURCES];
-  int64_t n_pages[GPB_MAX_GROUP_SOURCES];
-  int32_t n_src, page_bytes, parts, unit_begin;
+  ArenaTable<GPB_MAX_GROUP_SOURCES> tbl;
+  int32_t page_bytes, parts, unit_begin;
 };
 struct GatherGroupsArgs {
   GatherGroupArgs g[GPB_MAX_GROUPS];
@@ -42,6 +41,22 @@ struct RowGroupsArgs {
   int32_t n;
 };
 
+// A group's table from the caller's (n already checked against the group
+// capacity); unused entries stay zero.
+int fill_table(const gpb_sources &s, ArenaTable<GPB_MAX_GROUP_SOURCES> *t) {
+  for (int e = 0; e < s.n; ++e) {
+    if (s.n_pages[e] < 0) return GPB_EINVAL;
+    if (s.n_pages[e] > 0 && !s.base[e]) return GPB_EINVAL;
+    if (!aligned(s.base[e], 16)) return GPB_EALIGN;
+  }
+  t->n = s.n;
+  t->pad = 0;
+  for (int e = 0; e < GPB_MAX_GROUP_SOURCES; ++e)
+    t->e[e] = e < s.n ? ArenaEntry{static_cast<const uint8_t *>(s.base[e]), s.n_pages[e]}
+                      : ArenaEntry{nullptr, 0};
+  return GPB_OK;
+}
+
 template <typename Groups>
 __device__ __forceinline__ int group_of(const Groups &G, int unit) {
   int gi = 0;
@@ -54,8 +69,8 @@ __device__ __forceinline__ int group_of(const Groups &G, int unit) {
 // The gather of k_compose_gather, one 1 KiB unit per workgroup, for the
 // group the unit falls in.
 __global__ __launch_bounds__(kUnitLanes) void k_gather_groups(
-    GatherGroupsArgs G, const int32_t *__restrict__ owner,
-    const int32_t *__restrict__ src, int32_t *status) {
+    const int32_t *__restrict__ owner, const int32_t *__restrict__ src, int32_t *status,
+    GatherGroupsArgs G) {
   const int unit = blockIdx.x;
   const GatherGroupArgs &gr = G.g[group_of(G, unit)];
   const int u = unit - gr.unit_begin;
@@ -64,9 +79,9 @@ __global__ __launch_bounds__(kUnitLanes) void k_gather_groups(
   const int e = owner[slot];
   const int p = src[slot];
   const bool sentinel = (e < 0) || (p < 0);
-  const bool in_table = !sentinel && e < gr.n_src && p < gr.n_pages[e];
+  const bool in_table = !sentinel && e < gr.tbl.n && p < gr.tbl.e[e].n_pages;
   const uint8_t *from =
-      in_table ? gr.base[e] + static_cast<int64_t>(p) * gr.page_bytes : gr.dense;
+      in_table ? gr.tbl.e[e].base + static_cast<int64_t>(p) * gr.page_bytes : gr.dense;
   const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? gr.page_bytes : 0);
   const __amdgpu_buffer_rsrc_t rd =
       rsrc(gr.dense + static_cast<int64_t>(slot) * gr.page_bytes, gr.page_bytes);
@@ -79,7 +94,7 @@ __global__ __launch_bounds__(kUnitLanes) void k_gather_groups(
 // The scatter of k_row_scatter (one chunk per lane) for the group the
 // workgroup falls in.
 __global__ __launch_bounds__(kUnitLanes) void k_scatter_groups(
-    RowGroupsArgs G, const int32_t *__restrict__ rows, int32_t n_rows, int32_t *status) {
+    const int32_t *__restrict__ rows, int32_t n_rows, int32_t *status, RowGroupsArgs G) {
   const int unit = blockIdx.x;
   const RowGroupArgs &gr = G.g[group_of(G, unit)];
   const int rc = gr.row_chunks;
@@ -116,10 +131,9 @@ struct LayerGroupsArgs {
 };
 
 __global__ __launch_bounds__(kUnitLanes) void k_layer_groups(
-    LayerGroupsArgs G, const int32_t *__restrict__ pre_desc,
-    const int32_t *__restrict__ cur_desc, const int32_t *__restrict__ tok0,
-    const int32_t *__restrict__ ntok, const int32_t *__restrict__ rows, int32_t n_rows,
-    int32_t n_slots, int32_t *status) {
+    const int32_t *__restrict__ pre_desc, const int32_t *__restrict__ cur_desc,
+    const int32_t *__restrict__ tok0, const int32_t *__restrict__ ntok, int32_t *status,
+    int32_t n_slots, int32_t n_rows, const int32_t *__restrict__ rows, LayerGroupsArgs G) {
   const int unit = blockIdx.x;
   const bool is_cur = unit < G.n_cur_units;
   int gi = 0;
@@ -172,14 +186,7 @@ extern "C" int gpb_compose_layer_groups(const gpb_layer_group *groups, int32_t n
     const int64_t page_bytes = static_cast<int64_t>(page_rows) * q.row_bytes;
     if (page_bytes > INT32_MAX - (1 << 20)) return GPB_ERANGE;
     LayerGroupArgs &a = G.g[k];
-    a.tbl.n = q.table->n;
-    for (int e = 0; e < q.table->n; ++e) {
-      if (q.table->n_pages[e] < 0) return GPB_EINVAL;
-      if (q.table->n_pages[e] > 0 && !q.table->base[e]) return GPB_EINVAL;
-      if (!aligned(q.table->base[e], 16)) return GPB_EALIGN;
-      a.tbl.base[e] = static_cast<const uint8_t *>(q.table->base[e]);
-      a.tbl.n_pages[e] = q.table->n_pages[e];
-    }
+    if (int rc = fill_table(*q.table, &a.tbl)) return rc;
     const int64_t row_chunks = q.row_bytes / 16;
     const int64_t cur_bytes = static_cast<int64_t>(n_rows) * q.row_bytes;
     const int64_t staging_bytes = q.n_staging_rows * q.row_bytes;
@@ -219,9 +226,9 @@ extern "C" int gpb_compose_layer_groups(const gpb_layer_group *groups, int32_t n
     return GPB_EALIGN;
   if (units == 0) return GPB_OK;
   return launch(k_layer_groups, dim3(static_cast<uint32_t>(units)), dim3(kUnitLanes),
-                as_stream(stream), G, plan->d_prefix_desc, plan->d_current_desc,
-                plan->d_cur_page_token0, plan->d_cur_page_ntok, plan->d_staging_rows, n_rows,
-                n_slots, d_status);
+                as_stream(stream), plan->d_prefix_desc, plan->d_current_desc,
+                plan->d_cur_page_token0, plan->d_cur_page_ntok, d_status, n_slots, n_rows,
+                plan->d_staging_rows, G);
 }
 
 extern "C" int gpb_current_row_scatter_groups(const gpb_row_group *groups, int32_t n_groups,
@@ -260,7 +267,7 @@ extern "C" int gpb_current_row_scatter_groups(const gpb_row_group *groups, int32
   if (!d_staging_rows) return GPB_EINVAL;
   if (!aligned(d_staging_rows, 4)) return GPB_EALIGN;
   return launch(k_scatter_groups, dim3(static_cast<uint32_t>(units)), dim3(kUnitLanes),
-                as_stream(stream), G, d_staging_rows, n_rows, d_status);
+                as_stream(stream), d_staging_rows, n_rows, d_status, G);
 }
 
 extern "C" int gpb_compose_gather_groups(const gpb_gather_group *groups, int32_t n_groups,
@@ -283,14 +290,7 @@ extern "C" int gpb_compose_gather_groups(const gpb_gather_group *groups, int32_t
     const int64_t page_bytes = static_cast<int64_t>(page_rows) * q.row_bytes;
     if (page_bytes > INT32_MAX - (1 << 20)) return GPB_ERANGE;
     GatherGroupArgs &a = G.g[k];
-    a.n_src = q.table->n;
-    for (int e = 0; e < q.table->n; ++e) {
-      if (q.table->n_pages[e] < 0) return GPB_EINVAL;
-      if (q.table->n_pages[e] > 0 && !q.table->base[e]) return GPB_EINVAL;
-      if (!aligned(q.table->base[e], 16)) return GPB_EALIGN;
-      a.base[e] = static_cast<const uint8_t *>(q.table->base[e]);
-      a.n_pages[e] = q.table->n_pages[e];
-    }
+    if (int rc = fill_table(*q.table, &a.tbl)) return rc;
     if (n_slots == 0) continue;
     if (!q.d_dense) return GPB_EINVAL;
     if (!aligned(q.d_dense, 16)) return GPB_EALIGN;
@@ -305,5 +305,5 @@ extern "C" int gpb_compose_gather_groups(const gpb_gather_group *groups, int32_t
   if (!d_owner || !d_src) return GPB_EINVAL;
   if (!aligned(d_owner, 4) || !aligned(d_src, 4)) return GPB_EALIGN;
   return launch(k_gather_groups, dim3(static_cast<uint32_t>(units)), dim3(kUnitLanes),
-                as_stream(stream), G, d_owner, d_src, d_status);
+                as_stream(stream), d_owner, d_src, d_status, G);
 }

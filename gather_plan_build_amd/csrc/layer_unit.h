@@ -11,13 +11,19 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kScalarRows = 4;  // staging rows a workgroup may fetch as scalars
 
-// Source arenas of a pointer table, passed by value in the kernel arguments:
-// arena e starts at base[e] and holds n_pages[e] whole pages.
+// Source arenas of a pointer table, passed by value as the last kernel
+// argument: entry e (of n) starts at e[e].base and holds e[e].n_pages whole
+// pages.  The count and each entry's two fields sit side by side, so a unit
+// reads its entry from one line of the argument segment.
+struct ArenaEntry {
+  const uint8_t *base;
+  int64_t n_pages;
+};
 template <int N>
 struct ArenaTable {
-  const uint8_t *base[N];
-  int64_t n_pages[N];
   int32_t n;
+  int32_t pad;
+  ArenaEntry e[N];
 };
 
 // One unit of the layer's scatter and gather (page d63fbd4, commit "current
@@ -109,8 +115,8 @@ __device__ __forceinline__ void layer_unit(
     if (ok) wrote = staging + to;
   }
   const bool sentinel = (e < 0) || (p < 0);
-  const bool in_table = !sentinel && e < tbl.n && p < tbl.n_pages[e];
-  const uint8_t *from = in_table ? tbl.base[e] + static_cast<int64_t>(p) * page_bytes : dense;
+  const bool in_table = !sentinel && e < tbl.n && p < tbl.e[e].n_pages;
+  const uint8_t *from = in_table ? tbl.e[e].base + static_cast<int64_t>(p) * page_bytes : dense;
   const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
   const __amdgpu_buffer_rsrc_t rd =
       rsrc((is_cur ? dense : dense_pre) + static_cast<int64_t>(slot) * page_bytes, page_bytes);
