@@ -278,7 +278,7 @@ def _short(name):
     kept (they tell the gather from the slot-list gather, the scatter from the
     fused fill)."""
     import re
-    for key in ("k_compose_layer", "k_layer_groups", "k_compose_gather", "k_row_scatter",
+    for key in ("k_compose_layer_fill", "k_compose_layer", "k_layer_groups", "k_compose_gather", "k_row_scatter",
                 "k_gather_groups",
                 "k_scatter_groups", "k_fill_zero", "k_plan_scan_fill", "k_plan_slots",
                 "k_plan_tokens", "copyBuffer"):
@@ -341,6 +341,7 @@ def summarize_extras(trace_dir, workload="traced"):
              "# k_compose_gather<64,1,M>: M = 0 all slots, 1 slot list, 2 records (split "
              "halves); k_row_scatter<64,1,FILL,SROWS>: FILL = fused fill; "
              "k_compose_layer<64,SROWS>: one-launch layer, consume and layer-ahead launches; "
+             "k_compose_layer_fill<64,SROWS>: the one-launch layer with the fused fill; "
              "*_groups = token KV and index twin in one launch",
              "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
