@@ -21,7 +21,8 @@ STATUS_BAD_STAGING_ROW = 2
 STATUS_BAD_PLAN_INPUT = 4
 STATUS_LAYER_MISMATCH = 8
 
-OK, EINVAL, EALIGN, EPAGE, ECAPACITY, ERANGE, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, EALIGN, EPAGE, ECAPACITY, ERANGE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+SCRATCH_BYTES = 64 * 1024 * 1024  # GPB_SCRATCH_BYTES
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
@@ -116,6 +117,9 @@ def _load(path):
                                       ctypes.POINTER(gpb_plan), i32, i32, vp, i64, vp, i32,
                                       i32, i32, vp, vp]
     lib.gpb_compose_consume.argtypes = lib.gpb_compose_layer.argtypes
+    lib.gpb_compose_layer_noalloc.argtypes = [vp, ctypes.POINTER(gpb_sources), i32, i32,
+                                              ctypes.POINTER(gpb_plan), i32, i32, vp, i32,
+                                              i32, i32, vp, vp]
     lib.gpb_compose_layer_fill.argtypes = [vp, ctypes.POINTER(gpb_sources),
                                            ctypes.POINTER(gpb_plan), i32, i32, vp, i64, vp,
                                            i64, vp, i32, i32, i32, vp, vp]
@@ -146,7 +150,7 @@ EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_plan_build_clear",
            "gpb_writer_counts", "gpb_staging_clear", "gpb_current_row_scatter",
            "gpb_compose_gather", "gpb_compose_gather_slots", "gpb_compose_gather_records",
            "gpb_compose_layer", "gpb_compose_layer_fill", "gpb_compose_consume",
-           "gpb_compose_layer_ahead",
+           "gpb_compose_layer_ahead", "gpb_compose_layer_noalloc",
            "gpb_current_row_fill", "gpb_current_row_scatter_groups",
            "gpb_compose_gather_groups", "gpb_compose_layer_groups", "gpb_strerror")
 
@@ -402,6 +406,21 @@ def compose_layer(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging
                                  int(page_rows), int(row_bytes), _ptr(status),
                                  _stream(stream)),
            "gpb_compose_layer")
+
+
+def compose_layer_noalloc(dense, pools, n_writers, staging_cap_pages, plan, n_slots,
+                          n_cur_pages, cur_rows, n_rows, page_rows, row_bytes, status=None,
+                          stream=None):
+    """The one-launch layer with staging in the library's static array:
+    ``pools`` lists the pool entries only, the library adds the slabs."""
+    if not isinstance(pools, Sources):
+        pools = Sources(pools)
+    _check(lib.gpb_compose_layer_noalloc(_ptr(dense), ctypes.byref(pools.c), int(n_writers),
+                                         int(staging_cap_pages), ctypes.byref(plan.c),
+                                         int(n_slots), int(n_cur_pages), _ptr(cur_rows),
+                                         int(n_rows), int(page_rows), int(row_bytes),
+                                         _ptr(status), _stream(stream)),
+           "gpb_compose_layer_noalloc")
 
 
 def compose_layer_fill(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging_rows,

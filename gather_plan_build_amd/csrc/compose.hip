@@ -390,16 +390,17 @@ extern "C" int gpb_compose_gather_records(void *d_dense, const gpb_sources *tabl
 }
 
 namespace gpb {
-namespace {
 // The layer in one launch (with_prefix; prefix pages into d_dense_pre) or
 // its consume half only: the same kernel over all units, or over the current
-// pages' units alone.
+// pages' units alone.  With clear_staging, a launch of its own first zeroes
+// the whole staging region (all n_staging_rows rows), after every host check
+// has passed.
 int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
                   const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
                   void *d_staging, int64_t n_staging_rows, const void *d_cur_rows,
                   int32_t n_rows, int32_t page_rows, int32_t row_bytes, int32_t *d_status,
-                  void *stream, bool with_prefix, void *d_pool = nullptr,
-                  int64_t n_pool_rows = -1) {
+                  void *stream, bool with_prefix, void *d_pool, int64_t n_pool_rows,
+                  bool clear_staging) {
   const bool fill = n_pool_rows >= 0;
   constexpr int B = 64;
   SrcTable t;
@@ -441,6 +442,10 @@ int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
   const int32_t cur_units = static_cast<int32_t>(parts * n_cur_pages);
   void *const pre = with_prefix ? d_dense_pre : d_dense;
   const int32_t chunks = static_cast<int32_t>(row_chunks);
+  if (clear_staging && n_cur_pages > 0) {
+    const int rc_clear = gpb_staging_clear(d_staging, staging_bytes, stream);
+    if (rc_clear != GPB_OK) return rc_clear;
+  }
   if (fill)
     return launch(srows ? k_compose_layer_fill<B, true> : k_compose_layer_fill<B, false>, g, b,
                   as_stream(stream), plan->d_prefix_desc, plan->d_current_desc, cur_units,
@@ -454,7 +459,6 @@ int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
                 plan->d_cur_page_ntok, d_staging, staging_bytes, n_staging_rows,
                 plan->d_staging_rows, d_cur_rows, n_rows, chunks, t);
 }
-}  // namespace
 }  // namespace gpb
 
 extern "C" int gpb_compose_layer(void *d_dense, const gpb_sources *table,
@@ -464,7 +468,7 @@ extern "C" int gpb_compose_layer(void *d_dense, const gpb_sources *table,
                                  int32_t row_bytes, int32_t *d_status, void *stream) {
   return gpb::compose_layer(d_dense, d_dense, table, plan, n_slots, n_cur_pages, d_staging,
                             n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
-                            d_status, stream, true);
+                            d_status, stream, true, nullptr, -1, false);
 }
 
 extern "C" int gpb_compose_layer_fill(void *d_dense, const gpb_sources *table,
@@ -477,7 +481,7 @@ extern "C" int gpb_compose_layer_fill(void *d_dense, const gpb_sources *table,
   if (n_pool_rows < 0) return GPB_EINVAL;
   return gpb::compose_layer(d_dense, d_dense, table, plan, n_slots, n_cur_pages, d_staging,
                             n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
-                            d_status, stream, true, d_pool, n_pool_rows);
+                            d_status, stream, true, d_pool, n_pool_rows, false);
 }
 
 extern "C" int gpb_compose_layer_ahead(void *d_dense, void *d_dense_next,
@@ -488,7 +492,7 @@ extern "C" int gpb_compose_layer_ahead(void *d_dense, void *d_dense_next,
                                        int32_t *d_status, void *stream) {
   return gpb::compose_layer(d_dense, d_dense_next, table, plan, n_slots, n_cur_pages,
                             d_staging, n_staging_rows, d_cur_rows, n_rows, page_rows,
-                            row_bytes, d_status, stream, true);
+                            row_bytes, d_status, stream, true, nullptr, -1, false);
 }
 
 extern "C" int gpb_compose_consume(void *d_dense, const gpb_sources *table,
@@ -499,7 +503,7 @@ extern "C" int gpb_compose_consume(void *d_dense, const gpb_sources *table,
                                    int32_t *d_status, void *stream) {
   return gpb::compose_layer(d_dense, nullptr, table, plan, n_slots, n_cur_pages, d_staging,
                             n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
-                            d_status, stream, false);
+                            d_status, stream, false, nullptr, -1, false);
 }
 
 namespace gpb {
@@ -522,6 +526,7 @@ extern "C" const char *gpb_strerror(int status) {
     case GPB_ECAPACITY: return "staging capacity exceeded (slot 0 plus current pages)";
     case GPB_ERANGE: return "index or size does not fit in int32";
     case GPB_EHIP: return gpb::hip_error_text;
+    case GPB_ESCRATCH: return "staging would exceed the library's static scratch array";
     default: return "unknown gpb status";
   }
 }

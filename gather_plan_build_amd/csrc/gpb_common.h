@@ -51,4 +51,14 @@ int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// compose.hip: the one-launch layer (with_prefix) or its consume half, after
+// every host check; with d_pool and n_pool_rows >= 0 the fused fill, with
+// clear_staging a clear of all n_staging_rows staging rows launched first.
+int compose_layer(void *d_dense, void *d_dense_pre, const gpb_sources *table,
+                  const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
+                  void *d_staging, int64_t n_staging_rows, const void *d_cur_rows,
+                  int32_t n_rows, int32_t page_rows, int32_t row_bytes, int32_t *d_status,
+                  void *stream, bool with_prefix, void *d_pool, int64_t n_pool_rows,
+                  bool clear_staging);
+
 }  // namespace gpb

@@ -97,7 +97,9 @@ typedef enum gpb_status {
                           within the batch                                   */
   GPB_ECAPACITY = -4,  /* 1 + current pages > staging_cap_pages              */
   GPB_ERANGE = -5,     /* a row or element index would not fit in int32     */
-  GPB_EHIP = -6        /* the HIP runtime refused a launch                   */
+  GPB_EHIP = -6,       /* the HIP runtime refused a launch                   */
+  GPB_ESCRATCH = -7    /* gpb_compose_layer_noalloc: the staging region would
+                          exceed GPB_SCRATCH_BYTES                           */
 } gpb_status;
 
 /* Bits the kernels OR into the optional device status word (int32). */
@@ -494,6 +496,34 @@ int gpb_compose_layer_groups(const gpb_layer_group *groups, int32_t n_groups,
                              const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
                              int32_t n_rows, int32_t page_rows, int32_t *d_status,
                              void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * of gpb_compose_layer with its staging region taken from a static array of
+ * the library's own, GPB_SCRATCH_BYTES on each GPU (held from the first
+ * call on that GPU until the process ends), instead of a caller buffer.
+ * pools lists the NP pool entries only (1 <= NP <= GPB_MAX_SOURCES -
+ * n_writers); the library appends n_writers slabs of staging_cap_pages
+ * pages, carved from the array as gpb_plan_build assumes, and plan is a
+ * plan built for that geometry (n_writers, staging_cap_pages, page_rows).
+ * Each call zeroes the W * CAP * page_rows * row_bytes bytes it uses, in a
+ * launch of its own before the layer's (the array keeps the last call's
+ * rows), so the staging clear of gpb_plan_build_clear is not needed.  The
+ * work runs on the calling thread's current device, which `stream` must
+ * belong to.  Calls that overlap on one GPU share its array and race;
+ * calls in stream order do not.  Calls no allocating routine; the first
+ * call on a device looks the array's address up once.  Errors as
+ * gpb_compose_layer, plus GPB_ESCRATCH (n_writers * staging_cap_pages *
+ * page_rows * row_bytes > GPB_SCRATCH_BYTES), GPB_EINVAL (pools NULL, NP or
+ * n_writers out of range, staging_cap_pages < 1, a stream of another
+ * device) and GPB_EHIP (no device, or the address lookup failed). */
+#define GPB_SCRATCH_BYTES (64LL * 1024 * 1024)
+
+int gpb_compose_layer_noalloc(void *d_dense, const gpb_sources *pools, int32_t n_writers,
+                              int32_t staging_cap_pages, const gpb_plan *plan,
+                              int32_t n_slots, int32_t n_cur_pages, const void *d_cur_rows,
+                              int32_t n_rows, int32_t page_rows, int32_t row_bytes,
+                              int32_t *d_status, void *stream);
 
 /* Static, human-readable name of a gpb_status value. */
 const char *gpb_strerror(int status);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_names_every_status():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert gpb.strerror(code) and "unknown" not in gpb.strerror(code)
     assert "unknown" in gpb.strerror(-99)
 
@@ -207,6 +207,36 @@ def test_one_launch_layer_argument_checks():
         q.d_current_desc = None
         assert f(a, ctypes.byref(good.c), ctypes.byref(q), 4, 1, a, 10, a, 5, 64, 1152,
                  None, None) == B.EINVAL
+
+
+def test_noalloc_layer_argument_checks():
+    """Everything the static-staging layer can refuse without a device is
+    refused on the host: the table of pool entries, the writer count, the row
+    size and staging beyond GPB_SCRATCH_BYTES (GPB_ESCRATCH)."""
+    a = 0x100000
+    f = B.lib.gpb_compose_layer_noalloc
+    p = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
+    pools = B.Sources([(a, 10)])
+    full = B.Sources([(a, 10)] * B.MAX_SOURCES)
+
+    def call(pool_table, W, CAP, PS=64, RB=1152):
+        # dense, pools, W, CAP, plan, S, NCP, cur, T, PS, RB, status, stream
+        return f(a, None if pool_table is None else ctypes.byref(pool_table.c), W, CAP,
+                 ctypes.byref(p), 4, 1, a, 5, PS, RB, None, None)
+
+    assert call(None, 1, 4) == B.EINVAL
+    assert call(pools, 0, 4) == B.EINVAL                       # no writer
+    assert call(pools, 1, 0) == B.EINVAL                       # no staging page
+    assert call(full, 1, 4) == B.EINVAL                        # 64 pools + 1 slab
+    assert call(B.Sources([(a, 10)] * 60), 5, 4) == B.EINVAL
+    assert call(pools, 1, 4, PS=0) == B.EINVAL
+    assert call(pools, 1, 4, RB=1000) == B.EALIGN
+    rows_max = B.SCRATCH_BYTES // 1152
+    assert call(pools, 1, rows_max // 64 + 1) == B.ESCRATCH     # one slab too large
+    assert call(pools, 8, rows_max // 64 // 8 + 1) == B.ESCRATCH
+    assert call(pools, 1, 1 << 30, PS=1 << 30, RB=16) == B.ESCRATCH  # no overflow
+    assert call(pools, 63, (1 << 31) - 1, PS=(1 << 31) - 1, RB=16) == B.ESCRATCH
+    assert "scratch" in gpb.strerror(B.ESCRATCH)
 
 
 def test_layer_groups_argument_checks():

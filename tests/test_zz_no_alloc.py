@@ -1,0 +1,82 @@
+"""The one-launch layer for callers that cannot allocate device memory
+(gpb_compose_layer_noalloc: staging in the library's static array) against
+gpb_compose_layer with a caller-allocated staging region, and against the
+oracle, byte for byte.  Two calls in a row, the second on a smaller batch:
+the array still holds the first call's rows where the second batch's tail
+rows are read back, so a call that skipped its clear would show."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+POISON = 0xA5
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _layer_both_ways(gpb, b, orc):
+    """Dense of layer 0 through gpb_compose_layer (caller staging) and through
+    gpb_compose_layer_noalloc, each into a poisoned buffer, plus the oracle's."""
+    pools, curs = workloads.make_values(b, device="cuda")
+    meta = gpb.BatchMeta.of(b)
+    r = gpb.ComposeRunner(meta, pools, curs)
+    r.begin_batch()
+    r.dense[0].fill_(POISON)
+    r.layer(0)
+    dense = torch.full_like(r.dense[0], POISON)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    table = [(pools[0], b.n_pool_pages)] * b.n_pool_entries
+    gpb.compose_layer_noalloc(dense, table, b.n_writers, b.staging_cap_pages, r.plan, r.S,
+                              r.plan.NCP, curs[0], r.T, b.page_size, b.row_bytes, status)
+    torch.cuda.synchronize()
+    assert int(r.status.item()) == 0 and int(status.item()) == 0
+    want_plan = oracle.plan_for(b, orc)
+    staging = np.zeros(b.staging_rows_total * b.row_bytes, np.uint8)
+    want, bad = oracle.layer_for(b, want_plan, pools[0].cpu().numpy().reshape(-1),
+                                 curs[0].cpu().numpy(), staging, orc)
+    assert not bad
+    return r.dense[0].cpu().numpy(), dense.cpu().numpy(), want.reshape(-1)
+
+
+def test_noalloc_layer_matches_the_caller_staging_layer(orc):
+    import gather_plan_build_amd as gpb
+    big = workloads.make_batch("multi_source")
+    small = workloads.make_batch("tiny")
+    big_bytes = big.staging_rows_total * big.row_bytes
+    small_bytes = small.staging_rows_total * small.row_bytes
+    assert small_bytes < big_bytes <= gpb.binding.SCRATCH_BYTES
+    for b in (big, small):
+        _say("noalloc layer", b.name, "slots", b.n_req_pages, "rows", b.n_cur_tokens,
+             "writers", b.n_writers, "staging bytes", b.staging_rows_total * b.row_bytes)
+        caller, noalloc, want = _layer_both_ways(gpb, b, orc)
+        assert np.array_equal(caller, want), "%s: gpb_compose_layer differs" % b.name
+        if not np.array_equal(noalloc, caller):
+            rows = np.nonzero((noalloc.reshape(-1, b.row_bytes) !=
+                               caller.reshape(-1, b.row_bytes)).any(axis=1))[0]
+            raise AssertionError("%s: %d dense rows differ, first %s"
+                                 % (b.name, len(rows), rows[:8].tolist()))
+
+
+def test_noalloc_layer_refuses_staging_beyond_the_array():
+    """A geometry whose staging would not fit is refused before any launch:
+    the dense buffer keeps its poison."""
+    import gather_plan_build_amd as gpb
+    b = workloads.make_batch("tiny")
+    pools, curs = workloads.make_values(b, device="cuda")
+    r = gpb.ComposeRunner(gpb.BatchMeta.of(b), pools, curs)
+    r.begin_batch()
+    dense = torch.full_like(r.dense[0], POISON)
+    slab_bytes = b.page_size * b.row_bytes
+    too_many = gpb.binding.SCRATCH_BYTES // slab_bytes + 1
+    with pytest.raises(gpb.GpbError) as e:
+        gpb.compose_layer_noalloc(dense, [(pools[0], b.n_pool_pages)], 1, too_many, r.plan,
+                                  r.S, r.plan.NCP, curs[0], r.T, b.page_size, b.row_bytes)
+    assert e.value.code == gpb.binding.ESCRATCH
+    torch.cuda.synchronize()
+    assert (dense.cpu().numpy() == POISON).all()
