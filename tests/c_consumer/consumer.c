@@ -69,6 +69,10 @@ static int check(void) {
   bad |= expect(gpb_current_row_scatter(NULL, 8, NULL, NULL, 0, 1152, NULL, NULL),
                 GPB_OK, "empty scatter");
   bad |= expect(gpb_staging_clear(NULL, 0, NULL), GPB_OK, "empty clear");
+  t.n = 1;
+  bad |= expect(gpb_compose_layer_noalloc(NULL, &t, 1, (int32_t)(GPB_SCRATCH_BYTES / (64 * 1152)) + 1,
+                                          &p, 11, 3, NULL, 137, 64, 1152, NULL, NULL),
+                GPB_ESCRATCH, "staging beyond the static array");
   if (!bad) printf("c consumer: host checks ok\n");
   return bad;
 }
@@ -240,6 +244,21 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
               pass == 0 ? "one-launch layer" : pass == 1 ? "fused consume"
               : pass == 2 ? "layer ahead" : "grouped one-launch layer");
       return 11;
+    }
+  }
+
+  /* the one-launch layer with its staging in the library's static array:
+   * the pool entries only, the library adds the slabs */
+  {
+    gpb_sources pools = *t;
+    pools.n = b->n_pool_entries;
+    HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
+    CHECK(gpb_compose_layer_noalloc(d_dense2, &pools, b->n_writers, b->staging_cap_pages, p, S,
+                                    NCP, d_cur, T, b->page_size, b->row_bytes, d_status, st));
+    HCHECK(hipStreamSynchronize(st));
+    if (!same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+      fprintf(stderr, "layer with static staging differs from the two-call layer\n");
+      return 15;
     }
   }
 
