@@ -528,8 +528,11 @@ def main():
                       "parallelism": "single GPU",
                       "algorithmic_bytes_per_layer": layer_bytes}}
     # GPU-only regions, each behind a lead (see Lead): K*L back-to-back
-    # layers, and each kernel alone with the layer loop's arguments
-    reps = a.steps
+    # layers, and each kernel alone with the layer loop's arguments; a batch
+    # of few layers repeats its loop until a region holds at least
+    # MIN_REGION_LAYERS layers, so a region of microsecond launches is not
+    # a handful of calls
+    reps = max(a.steps, -(-MIN_REGION_LAYERS // L))
     lead = Lead(stream)
 
     def region(fn, calls_per_rep):
@@ -578,7 +581,7 @@ def main():
         a.twin_index_bytes = 0
     else:
         _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead)
-        out["ceilings"] = _ceilings(gpb, stream, lead, achieved)
+        out["ceilings"] = _ceilings(gpb, stream, lead, achieved, batch, layer_bytes)
     assert int(runner.status.item()) == 0
     if a.calibration_copy_mib:
         n = a.calibration_copy_mib << 20
@@ -592,11 +595,22 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _ceilings(gpb, stream, lead, achieved_gbs):
+MIN_REGION_LAYERS = 200
+
+# arenas cycled by the MALL-cold figure of one-layer workloads: 8 pools of
+# 1.2 GB, far beyond the 256 MB MALL
+COLD_ROTATIONS = 8
+
+
+def _ceilings(gpb, stream, lead, achieved_gbs, batch, layer_bytes):
     """What plain streams reach on this GPU, as context for the roofline
     fraction: a write-only fill (the library's staging clear) and a torch
     device copy (read + write), each over 1 GiB buffers, four times what the
-    256 MB MALL holds, in GPU-only regions."""
+    256 MB MALL holds, in GPU-only regions; and a copy of the layer's own
+    size -- the gather over contiguous pages of the workload's page size,
+    reading and writing layer_bytes / 2 bytes each per launch -- cycled over
+    enough buffer pairs that the MALL holds none of them, since a launch of
+    tens of MB pays its ramp and tail on fewer bytes than a 1 GiB stream."""
     import torch
     n, reps = 1 << 30, 10
     x = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -605,12 +619,34 @@ def _ceilings(gpb, stream, lead, achieved_gbs):
                      lead=lead(reps))
     copy_ms = _timed(stream, lambda: y.copy_(x), reps, lead=lead(reps))
     del x, y
+    page = batch.page_size * batch.row_bytes
+    pages = max(1, layer_bytes // 2 // page)
+    k = max(1, min(64, (2 << 30) // (pages * page)))
+    srcs = [torch.ones(pages * page, dtype=torch.uint8, device="cuda") for _ in range(k)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    tables = [gpb.Sources([(t, pages)]) for t in srcs]
+    owner = torch.zeros(pages, dtype=torch.int32, device="cuda")
+    src = torch.arange(pages, dtype=torch.int32, device="cuda")
+    calls = k * max(1, -(-40 // k))
+
+    def copies():
+        for i in range(calls):
+            gpb.compose_gather(dsts[i % k], tables[i % k], owner, src, pages,
+                               batch.page_size, batch.row_bytes, stream=stream)
+
+    same_ms = _timed(stream, copies, 1, lead=lead(calls)) / calls
+    del srcs, dsts, tables
     torch.cuda.empty_cache()
     fill_gbs = n / (fill_ms * 1e-3) / 1e9
+    same_gbs = 2 * pages * page / (same_ms * 1e-3) / 1e9
     return {"buffer_bytes": n,
             "fill_write_gbs": round(fill_gbs, 1),
             "torch_copy_read_write_gbs": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
-            "compose_layer_over_fill": round(achieved_gbs / fill_gbs, 4)}
+            "compose_layer_over_fill": round(achieved_gbs / fill_gbs, 4),
+            "layer_size_copy": {"bytes_per_launch": 2 * pages * page, "buffer_pairs": k,
+                                "us": round(same_ms * 1e3, 2),
+                                "read_write_gbs": round(same_gbs, 1)},
+            "compose_layer_over_layer_size_copy": round(achieved_gbs / same_gbs, 4)}
 
 
 def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
@@ -677,6 +713,22 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
         "serial_one_launch_ms_per_step": round(serial_ms, 4)}
     out["writer_scatters"] = {"writers": W, "us_per_layer": round(wsc_ms * 1e3, 2),
                               "single_scatter_us": round(s_ms * 1e3, 2)}
+    if batch.n_rotations == 1:
+        # a workload that repeats one layer over the same arenas reads pool
+        # pages the 256 MB MALL already holds: the same layer again over
+        # COLD_ROTATIONS distinct pool and current-row arenas, cycled
+        cpools, ccurs = workloads.make_values(batch, device="cuda",
+                                              rotations=COLD_ROTATIONS, seed=batch.seed + 2)
+        cold = gpb.ComposeRunner(gpb.BatchMeta.of(batch), cpools, ccurs, plan=runner.plan)
+        cold.begin_batch(stream)
+        R = COLD_ROTATIONS
+        cold_ms = region(lambda: [cold.layer(l, stream) for l in range(R)], R) / R
+        cold_b = cold.algorithmic_bytes_per_layer()
+        out["mall_cold"] = {"rotations": R, "us_per_layer": round(cold_ms * 1e3, 2),
+                            "pct_of_peak": round(100.0 * cold_b / (cold_ms * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBS, 2)}
+        assert int(cold.status.item()) == 0
+        del cold, cpools, ccurs
     if a.twin_index_bytes:
         rb = a.twin_index_bytes
         ipools, icurs = workloads.make_values(batch, device="cuda", row_bytes=rb,
