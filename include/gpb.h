@@ -512,7 +512,8 @@ int gpb_compose_layer_groups(const gpb_layer_group *groups, int32_t n_groups,
  * work runs on the calling thread's current device, which `stream` must
  * belong to.  Calls that overlap on one GPU share its array and race;
  * calls in stream order do not.  Calls no allocating routine; the first
- * call on a device looks the array's address up once.  Errors as
+ * call on a device looks the array's address up once, so make it before
+ * capturing a graph; later calls can be captured (two kernel nodes).  Errors as
  * gpb_compose_layer, plus GPB_ESCRATCH (n_writers * staging_cap_pages *
  * page_rows * row_bytes > GPB_SCRATCH_BYTES), GPB_EINVAL (pools NULL, NP or
  * n_writers out of range, staging_cap_pages < 1, a stream of another

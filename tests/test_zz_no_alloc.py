@@ -80,3 +80,55 @@ def test_noalloc_layer_refuses_staging_beyond_the_array():
     assert e.value.code == gpb.binding.ESCRATCH
     torch.cuda.synchronize()
     assert (dense.cpu().numpy() == POISON).all()
+
+
+def test_noalloc_layer_on_a_side_stream_and_in_a_graph(orc):
+    import gather_plan_build_amd as gpb
+    b = workloads.make_batch("medium")
+    pools, curs = workloads.make_values(b, device="cuda")
+    meta = gpb.BatchMeta.of(b)
+    r = gpb.ComposeRunner(meta, pools, curs)
+    r.begin_batch()
+    torch.cuda.synchronize()
+    want_plan = oracle.plan_for(b, orc)
+    staging = np.zeros(b.staging_rows_total * b.row_bytes, np.uint8)
+    want, bad = oracle.layer_for(b, want_plan, pools[0].cpu().numpy().reshape(-1),
+                                 curs[0].cpu().numpy(), staging, orc)
+    assert not bad
+    want = want.reshape(-1)
+    table = gpb.Sources([(pools[0], b.n_pool_pages)] * b.n_pool_entries)
+    dense = torch.full_like(r.dense[0], POISON)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def call(stream):
+        gpb.compose_layer_noalloc(dense, table, b.n_writers, b.staging_cap_pages, r.plan,
+                                  r.S, r.plan.NCP, curs[0], r.T, b.page_size, b.row_bytes,
+                                  status, stream)
+
+    print("eager call on a side stream", flush=True)
+    call(side)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert np.array_equal(dense.cpu().numpy(), want)
+
+    print("capture", flush=True)
+    graph = torch.cuda.CUDAGraph()
+    dense.fill_(POISON)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        call(side)
+    torch.cuda.synchronize()
+    for k in range(3):
+        # eager work between replays: the caller-staging layer over the same
+        # pool and a refill of the output with the poison byte
+        r.layer(0)
+        dense.fill_(POISON)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print("replay", k, flush=True)
+        assert int(status.item()) == 0
+        assert np.array_equal(dense.cpu().numpy(), want), "replay %d differs" % k
+    del graph
