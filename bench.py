@@ -34,7 +34,8 @@ METRIC = ("compose µs/layer and achieved HBM GB/s (% of peak) at bs=12, "
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    # 1000 traced steps are about 7 s of timed GPU work
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="traced",
                     choices=["traced", "opaque", "medium", "multi_source", "tiny"])
@@ -515,9 +516,16 @@ def main():
 
     layer_bytes = runner.algorithmic_bytes_per_layer()
     value_gbs = layer_bytes * L / (ms_per_step * 1e-3) / 1e9
+    lead = Lead(stream)
+    # the median of single steps, each in a region of its own behind a lead
+    # (a step of a one-layer batch is shorter than its host calls)
+    one_ms = sorted(_timed(stream, step, 1, lead=lead(L + 3)) for _ in range(MEDIAN_STEPS))
+    median_ms = 0.5 * (one_ms[(MEDIAN_STEPS - 1) // 2] + one_ms[MEDIAN_STEPS // 2])
     out = {"metric": METRIC, "value": round(value_gbs, 1), "unit": "GB/s",
            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "ms_per_step": round(ms_per_step, 4),
+           "ms_per_step_median": round(median_ms, 4), "median_of_steps": MEDIAN_STEPS,
+           "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
            "config": {"workload": "%s: bs=%d, %d current tokens, %d dense slots, "
                                   "%d-token pages, %d-byte rows, %d layers, plan once "
@@ -532,8 +540,7 @@ def main():
     # of few layers repeats its loop until a region holds at least
     # MIN_REGION_LAYERS layers, so a region of microsecond launches is not
     # a handful of calls
-    reps = max(a.steps, -(-MIN_REGION_LAYERS // L))
-    lead = Lead(stream)
+    reps = max(min(a.steps, MAX_REGION_REPS), -(-MIN_REGION_LAYERS // L))
 
     def region(fn, calls_per_rep):
         return _timed(stream, fn, reps, lead=lead(reps * calls_per_rep))
@@ -596,6 +603,8 @@ def main():
 
 
 MIN_REGION_LAYERS = 200
+MAX_REGION_REPS = 20      # repetitions of a many-layer loop per extra region
+MEDIAN_STEPS = 10         # steps timed one by one for the median
 
 # arenas cycled by the MALL-cold figure of one-layer workloads: 8 pools of
 # 1.2 GB, far beyond the 256 MB MALL
