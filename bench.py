@@ -628,7 +628,26 @@ def _ceilings(gpb, stream, lead, achieved_gbs, batch, layer_bytes):
                      lead=lead(reps))
     copy_ms = _timed(stream, lambda: y.copy_(x), reps, lead=lead(reps))
     del x, y
-    page = batch.page_size * batch.row_bytes
+    same = _layer_size_copy(gpb, stream, lead, batch.page_size, batch.row_bytes, layer_bytes)
+    torch.cuda.empty_cache()
+    fill_gbs = n / (fill_ms * 1e-3) / 1e9
+    return {"buffer_bytes": n,
+            "fill_write_gbs": round(fill_gbs, 1),
+            "torch_copy_read_write_gbs": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "compose_layer_over_fill": round(achieved_gbs / fill_gbs, 4),
+            "layer_size_copy": same,
+            "compose_layer_over_layer_size_copy": round(achieved_gbs / same["read_write_gbs"],
+                                                        4)}
+
+
+def _layer_size_copy(gpb, stream, lead, page_rows, row_bytes, layer_bytes):
+    """The library's gather over contiguous pages of page_rows x row_bytes,
+    reading and writing layer_bytes / 2 bytes each per launch, cycled over
+    enough buffer pairs (2 GiB of sources at least) that the MALL holds none
+    of them: what a launch of the layer's size reaches, ramp and tail
+    included."""
+    import torch
+    page = page_rows * row_bytes
     pages = max(1, layer_bytes // 2 // page)
     k = max(1, min(64, (2 << 30) // (pages * page)))
     srcs = [torch.ones(pages * page, dtype=torch.uint8, device="cuda") for _ in range(k)]
@@ -640,22 +659,13 @@ def _ceilings(gpb, stream, lead, achieved_gbs, batch, layer_bytes):
 
     def copies():
         for i in range(calls):
-            gpb.compose_gather(dsts[i % k], tables[i % k], owner, src, pages,
-                               batch.page_size, batch.row_bytes, stream=stream)
+            gpb.compose_gather(dsts[i % k], tables[i % k], owner, src, pages, page_rows,
+                               row_bytes, stream=stream)
 
-    same_ms = _timed(stream, copies, 1, lead=lead(calls)) / calls
+    ms = _timed(stream, copies, 1, lead=lead(calls)) / calls
     del srcs, dsts, tables
-    torch.cuda.empty_cache()
-    fill_gbs = n / (fill_ms * 1e-3) / 1e9
-    same_gbs = 2 * pages * page / (same_ms * 1e-3) / 1e9
-    return {"buffer_bytes": n,
-            "fill_write_gbs": round(fill_gbs, 1),
-            "torch_copy_read_write_gbs": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
-            "compose_layer_over_fill": round(achieved_gbs / fill_gbs, 4),
-            "layer_size_copy": {"bytes_per_launch": 2 * pages * page, "buffer_pairs": k,
-                                "us": round(same_ms * 1e3, 2),
-                                "read_write_gbs": round(same_gbs, 1)},
-            "compose_layer_over_layer_size_copy": round(achieved_gbs / same_gbs, 4)}
+    return {"bytes_per_launch": 2 * pages * page, "buffer_pairs": k, "us": round(ms * 1e3, 2),
+            "read_write_gbs": round(2 * pages * page / (ms * 1e-3) / 1e9, 1)}
 
 
 def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
@@ -773,7 +783,13 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
                              "token_and_twin_grouped_two_launch_us": round(both2_ms * 1e3,
                                                                            2)}
         assert int(twin.status.item()) == 0
-        del ipools, icurs, twin
+        del ipools, icurs
+        twin_copy = _layer_size_copy(gpb, stream, lead, batch.page_size, rb, tb)
+        out["index_twin"]["layer_size_copy"] = twin_copy
+        out["index_twin"]["over_layer_size_copy"] = round(
+            tb / (t_ms * 1e-3) / 1e9 / twin_copy["read_write_gbs"], 4)
+        del twin
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
