@@ -132,3 +132,29 @@ def test_noalloc_layer_on_a_side_stream_and_in_a_graph(orc):
         assert int(status.item()) == 0
         assert np.array_equal(dense.cpu().numpy(), want), "replay %d differs" % k
     del graph
+
+
+def test_noalloc_layer_fills_the_whole_array(orc):
+    """Staging of exactly GPB_SCRATCH_BYTES: one slab of 1,024 pages of 64
+    rows of 1,024 bytes, 1,023 current pages.  A first batch fills every row
+    of the array's top page with current rows; the second batch's last page
+    there is partial, so its 50 tail rows must read back as the zeros of the
+    second call's clear, not as the first call's rows."""
+    import gather_plan_build_amd as gpb
+    PS, RB, CAP = 64, 1024, 1024
+    assert CAP * PS * RB == gpb.binding.SCRATCH_BYTES
+    rng = np.random.default_rng(77)
+    n_pool = 4096
+    for tail in (0, 50):
+        P = np.array([3, 0], np.int32)
+        c = np.array([600 * PS + 5, 422 * PS - tail], np.int32)  # 601 + 422 current pages
+        n_cur_pages = int(sum((x + PS - 1) // PS for x in c))
+        assert n_cur_pages == CAP - 1
+        pages = rng.choice(np.arange(1, n_pool), size=int(P.sum()) + n_cur_pages,
+                           replace=False).astype(np.int32)
+        b = workloads.Batch("full_array", 2, PS, RB, n_pool, 1, 1, CAP, P, c, pages,
+                            value_kind="bytes", seed=77 + tail)
+        _say("noalloc layer over the whole array, last page short by", tail)
+        caller, noalloc, want = _layer_both_ways(gpb, b, orc)
+        assert np.array_equal(caller, want)
+        assert np.array_equal(noalloc, caller), "tail %d: the layer differs" % tail
