@@ -122,9 +122,10 @@ __device__ __forceinline__ void layer_unit(
   // Pool pages are streamed.  A current page's bytes were just written by
   // this very wave: they are read back through the cache at the address the
   // table gives (from + off), formed from the staging region's own buffer
-  // resource, the one the scatter's stores used, whenever that address lies
-  // inside the staging region for every lane (always, under the layout
+  // resource, the one the scatter's stores used, whenever the unit's KiB
+  // lies inside the staging region (always, under the layout
   // gpb_plan_build assumes); otherwise through the table entry's resource.
+  // The test is on the unit's whole KiB, so it is one scalar branch.
   // The bytes read are the same either way.  The resource and offset are
   // chosen before the load, so no temporary shares a register with a load
   // in flight and the read-back does not wait for the staging store.  Against
@@ -133,12 +134,14 @@ __device__ __forceinline__ void layer_unit(
   // with more of the read-back served by L2.
   __amdgpu_buffer_rsrc_t rb = rs;
   uint32_t ob = off;
-  if (is_cur) {
-    const int64_t rel = (from + off) - staging;
-    const bool inside = in_table && rel >= 0 && rel + 16 <= staging_bytes;
-    if (__all(inside)) {
+  if (is_cur && in_table) {
+    // where the unit's KiB of the page starts and ends within the staging
+    // region (uniform across the wave)
+    const int64_t rel0 = from - staging;
+    const int64_t end = rel0 + static_cast<int64_t>(part * B + B) * 16;
+    if (rel0 >= 0 && end <= staging_bytes) {
       rb = rsrc(staging, staging_bytes);
-      ob = static_cast<uint32_t>(rel);
+      ob = static_cast<uint32_t>(rel0) + off;
     }
   }
   const u32x4 back = is_cur ? ld16_staged(rb, ob) : ld16(rb, ob);
