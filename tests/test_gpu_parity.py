@@ -441,28 +441,61 @@ def test_shared_plan_must_match_the_batch(orc):
 
 
 def test_one_launch_layer_reports_a_table_that_breaks_the_layout(orc):
-    """The one-launch layer reads each current page back through the table;
-    a table whose staging entry is not the staging the rows are written to
-    is reported (GPB_STATUS_LAYER_MISMATCH), while the same call with the
-    plan's layout reports nothing."""
+    """The one-launch layer reads each current page back at the address the
+    table gives; a table whose staging entries are not the staging the rows
+    are written to is reported (GPB_STATUS_LAYER_MISMATCH), while the same
+    call with the plan's layout reports nothing.  Either way the current
+    pages hold the bytes at the table's address: read through the staging
+    region's resource when that address lies in the staging region (here its
+    second half, which the call does not write), through the table entry's
+    otherwise (a separate buffer); prefix pages and the scatter are as the
+    oracle's."""
     gpb = _gpb()
     b = workloads.make_batch("tiny")
     pools, curs = workloads.make_values(b, device="cuda")
     r = _runner(b, pools, curs)
     r.begin_batch()
+    torch.cuda.synchronize()
+    want_plan = _check_plan(b, r, orc)
+    want_dense, want_staging = _oracle_layer(b, want_plan, _host(pools[0]), _host(curs[0]), orc)
+    cur_slots = _host(r.plan.t["current_slots"])
+    page_rows = np.concatenate([np.arange(s * b.page_size, (s + 1) * b.page_size)
+                                for s in cur_slots])
+    prefix_rows = np.setdiff1d(np.arange(r.S * b.page_size), page_rows)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     good = r.tables[(0, 0)]
     gpb.compose_layer(r.dense[0], good, r.plan, r.S, r.plan.NCP, r.staging[0],
                       r.staging_rows_total, curs[0], r.T, r.ps, r.rb, status)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
-    elsewhere = torch.zeros_like(r.staging[0])
-    bad = gpb.Sources([(pools[0], b.n_pool_pages)] * b.n_pool_entries +
-                      [(elsewhere, b.staging_cap_pages)] * b.n_writers)
-    gpb.compose_layer(r.dense[0], bad, r.plan, r.S, r.plan.NCP, r.staging[0],
-                      r.staging_rows_total, curs[0], r.T, r.ps, r.rb, status)
-    torch.cuda.synchronize()
-    assert int(status.item()) == gpb.STATUS_LAYER_MISMATCH
+    assert np.array_equal(_host(r.dense_of(0)), want_dense)
+
+    slab = b.staging_cap_pages * b.page_size * b.row_bytes
+    elsewhere = torch.full_like(r.staging[0], 0x5A)
+    r.staging[1].fill_(0x3C)
+    second = r.staging[1].data_ptr()
+    pool_entries = [(pools[0], b.n_pool_pages)] * b.n_pool_entries
+    cases = [("a separate buffer", 0x5A, r.staging[0], r.staging_rows_total,
+              [(elsewhere.data_ptr() + w * slab, b.staging_cap_pages)
+               for w in range(b.n_writers)]),
+             ("the staging region's second half", 0x3C, r.staging_all,
+              2 * r.staging_rows_total,
+              [(second + w * slab, b.staging_cap_pages) for w in range(b.n_writers)])]
+    for what, byte, staging, n_staging_rows, slabs in cases:
+        _say("layer with the staging entries in", what)
+        r.staging_all.zero_()
+        r.staging[1].fill_(0x3C)
+        r.dense[0].fill_(POISON)
+        status.zero_()
+        bad = gpb.Sources(pool_entries + slabs)
+        gpb.compose_layer(r.dense[0], bad, r.plan, r.S, r.plan.NCP, staging, n_staging_rows,
+                          curs[0], r.T, r.ps, r.rb, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == gpb.STATUS_LAYER_MISMATCH, what
+        got = _host(r.dense_of(0))
+        assert (got[page_rows] == byte).all(), what
+        assert np.array_equal(got[prefix_rows], want_dense[prefix_rows]), what
+        assert np.array_equal(_host(r.staging_of(0)), want_staging), what
 
 
 def test_records_out_of_range_are_skipped(orc):
