@@ -29,6 +29,8 @@
 //     staging stores carry sc1 (their reader is the next kernel), the
 //     one-launch layer's staging stores and read-back the plain policy (the
 //     reader is the same wave), each measured fastest for its kernel here;
+//     the one-launch layer forms the read-back from the staging region's
+//     own resource, which L2 then serves for the most part;
 //   - raw buffer resources bound every access, so ragged tails, -1 sentinels
 //     and bad rows cost no branches;
 //   - kernel arguments come in the order a wave reads them, the first 14
