@@ -550,8 +550,10 @@ def main():
                     2 * L) / L
     g_ms = region(lambda: [runner.gather(l, stream) for l in range(L)], L) / L
     s_ms = region(lambda: [runner.scatter(l, stream) for l in range(L)], L) / L
-    # plan build with the staging clear: three launches per batch
+    # plan build with the staging clear: three launches per batch; and the
+    # plan build alone (gpb_plan_build, the same three launches, no clear)
     p_ms = region(lambda: runner.begin_batch(stream), 1)
+    p0_ms = region(lambda: runner.plan.build(stream), 1)
     # host time of one gpb_plan_build_clear call (validation + three
     # launches, no synchronisation), for comparison with host-side builders
     torch.cuda.synchronize()
@@ -572,7 +574,8 @@ def main():
     out["kernels_us"] = {"compose_layer": round(layer_ms * 1e3, 2),
                          "compose_gather": round(g_us, 2),
                          "current_row_scatter": round(s_us, 2),
-                         "plan_build_with_staging_clear": round(p_ms * 1e3, 2)}
+                         "plan_build_with_staging_clear": round(p_ms * 1e3, 2),
+                         "plan_build": round(p0_ms * 1e3, 2)}
     out["two_launch_layer"] = {
         "us_per_layer": round(two_ms * 1e3, 2),
         "pct_of_peak": round(100.0 * layer_bytes / (two_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
