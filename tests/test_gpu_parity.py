@@ -654,6 +654,74 @@ def test_full_pointer_table(orc):
     _random_case(orc, b)
 
 
+def _owner_arenas(b, pool):
+    """One pool arena per pool entry, as each rank would hold its own pool:
+    arena e keeps the pages p with p mod NP == e and holds the sentinel byte
+    everywhere else, so a page read through the wrong entry shows."""
+    page_bytes = b.page_size * b.row_bytes
+    owner = torch.from_numpy(np.arange(b.n_pool_pages) % b.n_pool_entries).cuda()
+    arenas = []
+    for e in range(b.n_pool_entries):
+        a = pool.clone().view(b.n_pool_pages, page_bytes)
+        a[owner != e] = POISON
+        arenas.append(a.view(-1))
+    return arenas
+
+
+@pytest.mark.parametrize("which", ["full_table", "multi_source"])
+def test_pool_entries_as_distinct_owner_arenas(orc, which):
+    """The pool entries of the table are distinct arenas, each holding only
+    the pages its entry owns (page mod NP), the rest poisoned: the one-launch
+    layer, the two-launch layer and the record split read every prefix page
+    from its owner's arena and match the oracle (which reads one pool)."""
+    gpb = _gpb()
+    b = _full_table_batch() if which == "full_table" else workloads.make_batch(which)
+    if which == "full_table":
+        pool_np, cur_np = pins.tagged_values(b)
+        pools, curs = [torch.from_numpy(pool_np).cuda()], [torch.from_numpy(cur_np).cuda()]
+    else:
+        pools, curs = workloads.make_values(b, device="cuda")
+        pool_np, cur_np = _host(pools[0]), _host(curs[0])
+    r = _runner(b, pools, curs)
+    r.begin_batch()
+    torch.cuda.synchronize()
+    want_plan = _check_plan(b, r, orc)
+    want, want_staging = _oracle_layer(b, want_plan, pool_np, cur_np, orc)
+    arenas = _owner_arenas(b, pools[0])
+    slab = b.staging_cap_pages * b.page_size * b.row_bytes
+    base = r.staging[0].data_ptr()
+    table = gpb.Sources([(a, b.n_pool_pages) for a in arenas] +
+                        [(base + w * slab, b.staging_cap_pages) for w in range(b.n_writers)])
+    NCP = r.plan.NCP
+    runs = {
+        "one launch": lambda: gpb.compose_layer(
+            r.dense[0], table, r.plan, r.S, NCP, r.staging[0], r.staging_rows_total, curs[0],
+            r.T, r.ps, r.rb, r.status),
+        "two launches": lambda: (
+            gpb.current_row_scatter(r.staging[0], r.staging_rows_total,
+                                    r.plan.t["staging_rows"], curs[0], r.T, r.rb, r.status),
+            gpb.compose_gather(r.dense[0], table, r.plan.t["owner"], r.plan.t["src"], r.S,
+                               r.ps, r.rb, r.status)),
+        "record split": lambda: (
+            gpb.compose_gather_records(r.dense[0], table, r.plan.t["prefix_desc"],
+                                       r.S - NCP, r.S, r.ps, r.rb, r.status),
+            gpb.compose_consume(r.dense[0], table, r.plan, r.S, NCP, r.staging[0],
+                                r.staging_rows_total, curs[0], r.T, r.ps, r.rb, r.status)),
+    }
+    for what, run in runs.items():
+        _say(which, what, "NP", b.n_pool_entries, "W", b.n_writers)
+        r.dense[0].fill_(POISON)
+        run()
+        torch.cuda.synchronize()
+        got = _host(r.dense_of(0))
+        if not np.array_equal(got, want):
+            bad_rows = np.nonzero((got != want).any(axis=1))[0]
+            raise AssertionError("%s, %s: %d dense rows differ, first %s"
+                                 % (which, what, len(bad_rows), bad_rows[:8].tolist()))
+        assert np.array_equal(_host(r.staging_of(0)), want_staging), what
+        assert _status(r) == 0, what
+
+
 def test_empty_and_degenerate_batches(orc):
     cases = [([], []), ([0, 0], [0, 0]), ([3, 2], [0, 0]), ([0, 0], [5, 64]),
              ([1], [65])]
