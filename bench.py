@@ -702,8 +702,11 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
         ms = region(lambda: runner.run_pipelined(L, stream, side, consume=consume),
                     4 * L + 2)
         pipe[consume] = ms
-    # the same schedule on one stream, one launch per layer
+    # the same schedule on one stream, one launch per layer; and with the
+    # fused fill in every consume
     ahead_ms = region(lambda: runner.run_layer_ahead(L, stream), L + 2)
+    ahead_fill_ms = region(lambda: runner.run_layer_ahead(L, stream, fill=True), L + 2)
+    cons_fill_ms = region(lambda: [runner.consume_fill(l, stream) for l in range(L)], L) / L
     serial_ms = region(lambda: runner.run(L, stream), L + 1)
     # the whole step captured once as a HIP graph and replayed: same kernels,
     # no per-launch host work
@@ -732,6 +735,8 @@ def _extras(a, out, runner, batch, stream, reps, L, s_ms, g_ms, lead):
         "pipelined_us_per_layer_incl_plan": round(pipe["fused"] * 1e3 / L, 2),
         "pipelined_scatter_consume_ms_per_step": round(pipe["scatter"], 4),
         "layer_ahead_one_launch_ms_per_step": round(ahead_ms, 4),
+        "layer_ahead_with_fused_fill_ms_per_step": round(ahead_fill_ms, 4),
+        "consume_fused_with_fill_us": round(cons_fill_ms * 1e3, 2),
         "serial_one_launch_ms_per_step": round(serial_ms, 4)}
     out["writer_scatters"] = {"writers": W, "us_per_layer": round(wsc_ms * 1e3, 2),
                               "single_scatter_us": round(s_ms * 1e3, 2)}

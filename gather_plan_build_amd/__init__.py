@@ -6,7 +6,8 @@ Importing this package loads libgpb.so and fails loudly if it is missing.
 from .binding import (BatchMeta, GpbError, Plan, Sources, compose_gather,  # noqa: F401
                       compose_gather_slots, compose_gather_records, compose_layer,
                       compose_consume, compose_layer_ahead, compose_layer_fill,
-                      compose_layer_noalloc,
+                      compose_layer_noalloc, compose_consume_fill,
+                      compose_layer_ahead_fill,
                       current_row_fill, writer_counts,
                       compose_gather_groups, compose_layer_groups,
                       current_row_scatter_groups,

@@ -124,6 +124,8 @@ def _load(path):
                                            ctypes.POINTER(gpb_plan), i32, i32, vp, i64, vp,
                                            i64, vp, i32, i32, i32, vp, vp]
     lib.gpb_compose_layer_ahead.argtypes = [vp] + list(lib.gpb_compose_layer.argtypes)
+    lib.gpb_compose_consume_fill.argtypes = lib.gpb_compose_layer_fill.argtypes
+    lib.gpb_compose_layer_ahead_fill.argtypes = [vp] + list(lib.gpb_compose_layer_fill.argtypes)
     lib.gpb_staging_clear.argtypes = [vp, i64, vp]
     lib.gpb_current_row_scatter.argtypes = [vp, i64, vp, vp, i32, i32, vp, vp]
     lib.gpb_compose_gather.argtypes = [vp, ctypes.POINTER(gpb_sources), vp, vp, i32,
@@ -151,6 +153,7 @@ EXPORTS = ("gpb_plan_sizes", "gpb_plan_build", "gpb_plan_build_clear",
            "gpb_compose_gather", "gpb_compose_gather_slots", "gpb_compose_gather_records",
            "gpb_compose_layer", "gpb_compose_layer_fill", "gpb_compose_consume",
            "gpb_compose_layer_ahead", "gpb_compose_layer_noalloc",
+           "gpb_compose_consume_fill", "gpb_compose_layer_ahead_fill",
            "gpb_current_row_fill", "gpb_current_row_scatter_groups",
            "gpb_compose_gather_groups", "gpb_compose_layer_groups", "gpb_strerror")
 
@@ -464,6 +467,38 @@ def compose_layer_ahead(dense, dense_next, sources, plan, n_slots, n_cur_pages, 
                                        int(n_rows), int(page_rows), int(row_bytes),
                                        _ptr(status), _stream(stream)),
            "gpb_compose_layer_ahead")
+
+
+def compose_consume_fill(dense, sources, plan, n_slots, n_cur_pages, staging, n_staging_rows,
+                         pool, n_pool_rows, cur_rows, n_rows, page_rows, row_bytes, status=None,
+                         stream=None):
+    """The consume half in one launch with the fused fill (current rows also
+    to their pool rows)."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_consume_fill(_ptr(dense), ctypes.byref(sources.c),
+                                        ctypes.byref(plan.c), int(n_slots), int(n_cur_pages),
+                                        _ptr(staging), int(n_staging_rows), _ptr(pool),
+                                        int(n_pool_rows), _ptr(cur_rows), int(n_rows),
+                                        int(page_rows), int(row_bytes), _ptr(status),
+                                        _stream(stream)),
+           "gpb_compose_consume_fill")
+
+
+def compose_layer_ahead_fill(dense, dense_next, sources, plan, n_slots, n_cur_pages, staging,
+                             n_staging_rows, pool, n_pool_rows, cur_rows, n_rows, page_rows,
+                             row_bytes, status=None, stream=None):
+    """This layer's consume with the fused fill and the next layer's prefix
+    pages in one launch."""
+    if not isinstance(sources, Sources):
+        sources = Sources(sources)
+    _check(lib.gpb_compose_layer_ahead_fill(_ptr(dense), _ptr(dense_next),
+                                            ctypes.byref(sources.c), ctypes.byref(plan.c),
+                                            int(n_slots), int(n_cur_pages), _ptr(staging),
+                                            int(n_staging_rows), _ptr(pool), int(n_pool_rows),
+                                            _ptr(cur_rows), int(n_rows), int(page_rows),
+                                            int(row_bytes), _ptr(status), _stream(stream)),
+           "gpb_compose_layer_ahead_fill")
 
 
 def current_row_fill(staging, n_staging_rows, staging_rows, pool, n_pool_rows, pool_locs,

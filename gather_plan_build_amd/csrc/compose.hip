@@ -508,6 +508,33 @@ extern "C" int gpb_compose_consume(void *d_dense, const gpb_sources *table,
                             d_status, stream, false, nullptr, -1, false);
 }
 
+extern "C" int gpb_compose_consume_fill(void *d_dense, const gpb_sources *table,
+                                        const gpb_plan *plan, int32_t n_slots,
+                                        int32_t n_cur_pages, void *d_staging,
+                                        int64_t n_staging_rows, void *d_pool,
+                                        int64_t n_pool_rows, const void *d_cur_rows,
+                                        int32_t n_rows, int32_t page_rows, int32_t row_bytes,
+                                        int32_t *d_status, void *stream) {
+  if (n_pool_rows < 0) return GPB_EINVAL;
+  return gpb::compose_layer(d_dense, nullptr, table, plan, n_slots, n_cur_pages, d_staging,
+                            n_staging_rows, d_cur_rows, n_rows, page_rows, row_bytes,
+                            d_status, stream, false, d_pool, n_pool_rows, false);
+}
+
+extern "C" int gpb_compose_layer_ahead_fill(void *d_dense, void *d_dense_next,
+                                            const gpb_sources *table, const gpb_plan *plan,
+                                            int32_t n_slots, int32_t n_cur_pages,
+                                            void *d_staging, int64_t n_staging_rows,
+                                            void *d_pool, int64_t n_pool_rows,
+                                            const void *d_cur_rows, int32_t n_rows,
+                                            int32_t page_rows, int32_t row_bytes,
+                                            int32_t *d_status, void *stream) {
+  if (n_pool_rows < 0) return GPB_EINVAL;
+  return gpb::compose_layer(d_dense, d_dense_next, table, plan, n_slots, n_cur_pages,
+                            d_staging, n_staging_rows, d_cur_rows, n_rows, page_rows,
+                            row_bytes, d_status, stream, true, d_pool, n_pool_rows, false);
+}
+
 namespace gpb {
 namespace {
 thread_local char hip_error_text[160] = "HIP launch failed";

@@ -178,14 +178,39 @@ class ComposeRunner:
                               self.staging_rows_total, self.curs[layer % len(self.curs)],
                               self.T, self.ps, self.rb, self.status, stream)
 
+    def consume_fill(self, layer, stream=None):
+        """The consume half in one launch with the fused fill: the current
+        rows also go to their pool rows in the layer's pool arena."""
+        h, k = layer % PARITY, layer % len(self.pools)
+        B.compose_consume_fill(self.dense[h], self.tables[(k, h)], self.plan, self.S,
+                               self.plan.NCP, self.staging[h], self.staging_rows_total,
+                               self.pools[k], self.n_pool_pages * self.ps,
+                               self.curs[layer % len(self.curs)], self.T, self.ps, self.rb,
+                               self.status, stream)
+
+    def ahead_fill(self, layer, stream=None):
+        """ahead() with the fused fill: layer l's current rows also go to
+        their pool rows in layer l's pool arena, while the table names layer
+        l + 1's pool entries for the prefix pages."""
+        h, hn = layer % PARITY, (layer + 1) % PARITY
+        k = (layer + 1) % len(self.pools)
+        B.compose_layer_ahead_fill(self.dense[h], self.dense[hn], self.tables[(k, h)],
+                                   self.plan, self.S, self.plan.NCP, self.staging[h],
+                                   self.staging_rows_total, self.pools[layer % len(self.pools)],
+                                   self.n_pool_pages * self.ps,
+                                   self.curs[layer % len(self.curs)], self.T, self.ps,
+                                   self.rb, self.status, stream)
+
     def run_layer_ahead(self, n_layers, stream=None, before_prefetch=None,
-                        after_consume=None):
+                        after_consume=None, fill=False):
         """The batch with the layer-ahead prefetch on one stream, one launch
         per layer: the prefix pages of layer 0, then for each layer l its
         consume together with the prefix pages of layer l + 1
         (gpb_compose_layer_ahead), the last layer's consume alone.  The dense
         half layer l + 1 fills was last read by layer l - 1, whose launch
-        came before.  Hooks as in run_pipelined, both on ``stream``."""
+        came before.  With ``fill`` every consume also stores the layer's
+        current rows at their pool rows (the _fill launches).  Hooks as in
+        run_pipelined, both on ``stream``."""
         self.begin_batch(stream)
         if n_layers == 0:
             return
@@ -196,9 +221,9 @@ class ComposeRunner:
             if l + 1 < n_layers:
                 if before_prefetch is not None:
                     before_prefetch(l + 1, stream)
-                self.ahead(l, stream)
+                (self.ahead_fill if fill else self.ahead)(l, stream)
             else:
-                self.consume_fused(l, stream)
+                (self.consume_fill if fill else self.consume_fused)(l, stream)
             if after_consume is not None:
                 after_consume(l, stream)
 

@@ -12,7 +12,8 @@
  * in one launch.  The layer-ahead split gathers a layer's prefix pages
  * early (gpb_compose_gather_records) and its current pages at consume time
  * (gpb_compose_consume), or layer l's consume together with layer l + 1's
- * prefix pages (gpb_compose_layer_ahead).
+ * prefix pages (gpb_compose_layer_ahead); the _fill variants also store the
+ * current rows in the KV cache.
  *
  * Where the method comes from (commit pages of the sglang fork, cited by the
  * page's commit hash and the commit's subject):
@@ -432,6 +433,31 @@ int gpb_compose_layer_ahead(void *d_dense, void *d_dense_next, const gpb_sources
                             void *d_staging, int64_t n_staging_rows, const void *d_cur_rows,
                             int32_t n_rows, int32_t page_rows, int32_t row_bytes,
                             int32_t *d_status, void *stream);
+
+/* The consume and layer-ahead launches with the fused fill (page 0d87bc5,
+ * commit "prefetch staging exchange": the consume step fills the current
+ * rows; page d63fbd4, commit "current rows written straight into staging":
+ * the fill goes to the KV cache and to staging in one pass): as
+ * gpb_compose_consume and gpb_compose_layer_ahead, with each current row
+ * also written to its pool row plan->d_pool_locs[t] of d_pool (this layer's
+ * pool, n_pool_rows rows), as gpb_compose_layer_fill does.  In the
+ * layer-ahead call the table's pool entries are the next layer's pools and
+ * d_pool is this layer's; the pool rows written are current tokens' own,
+ * never pages a gather reads.  Errors as gpb_compose_consume /
+ * gpb_compose_layer_ahead, plus those gpb_compose_layer_fill adds for the
+ * pool. */
+int gpb_compose_consume_fill(void *d_dense, const gpb_sources *table, const gpb_plan *plan,
+                             int32_t n_slots, int32_t n_cur_pages, void *d_staging,
+                             int64_t n_staging_rows, void *d_pool, int64_t n_pool_rows,
+                             const void *d_cur_rows, int32_t n_rows, int32_t page_rows,
+                             int32_t row_bytes, int32_t *d_status, void *stream);
+
+int gpb_compose_layer_ahead_fill(void *d_dense, void *d_dense_next, const gpb_sources *table,
+                                 const gpb_plan *plan, int32_t n_slots, int32_t n_cur_pages,
+                                 void *d_staging, int64_t n_staging_rows, void *d_pool,
+                                 int64_t n_pool_rows, const void *d_cur_rows, int32_t n_rows,
+                                 int32_t page_rows, int32_t row_bytes, int32_t *d_status,
+                                 void *stream);
 
 /* Several row formats composed on one plan in one launch each (page 0d87bc5,
  * commit "prefetch staging exchange": the indexer-key fill reuses the token

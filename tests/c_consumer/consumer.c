@@ -143,25 +143,56 @@ static int other_entry_points(const gpb_batch *b, const gpb_plan *p, const gpb_s
     }
   }
 
-  /* the one-launch layer with the fused fill into a copy of the pool: same
-   * dense and staging; the pool is checked with the separate fill below */
+  /* the launches with the fused fill, each into a fresh copy of the pool:
+   * the one-launch layer, the prefix records then the consume with fill,
+   * and the layer-ahead launch with fill (the "next" layer's prefix pages
+   * into the same buffer through a separate pointer).  Same dense and
+   * staging as the two-call layer; the same pool as the first of them,
+   * which is checked with the separate fill below */
   {
     gpb_sources t3 = *t;
     for (int w = 0; w < b->n_writers; w++)
       t3.base[b->n_pool_entries + w] =
           (uint8_t *)d_stag2 + (size_t)w * b->staging_cap_pages * PS * RB;
-    HCHECK(hipMemcpy(d_pool2, d_pool, pool_bytes, hipMemcpyDeviceToDevice));
-    CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
-    HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
-    CHECK(gpb_compose_layer_fill(d_dense2, &t3, p, S, NCP, d_stag2, (int64_t)stag_rows,
-                                 d_pool2, (int64_t)(b->n_pool_pages * PS), d_cur, T,
-                                 b->page_size, b->row_bytes, d_status, st));
-    HCHECK(hipStreamSynchronize(st));
-    if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB) ||
-        !same_device_bytes(d_dense2, d_dense, dense_bytes)) {
-      fprintf(stderr, "one-launch layer with fill differs from the two-call layer\n");
-      return 14;
+    const int64_t pool_rows = (int64_t)b->n_pool_pages * (int64_t)PS;
+    void *d_pool3;
+    HCHECK(hipMalloc(&d_pool3, pool_bytes));
+    for (int pass = 0; pass < 3; pass++) {
+      HCHECK(hipMemcpy(d_pool2, d_pool, pool_bytes, hipMemcpyDeviceToDevice));
+      CHECK(gpb_staging_clear(d_stag2, (int64_t)(stag_rows * RB), st));
+      HCHECK(hipMemsetAsync(d_dense2, 0xEE, dense_bytes + 16, st));
+      if (pass == 0) {
+        CHECK(gpb_compose_layer_fill(d_dense2, &t3, p, S, NCP, d_stag2, (int64_t)stag_rows,
+                                     d_pool2, pool_rows, d_cur, T, b->page_size, b->row_bytes,
+                                     d_status, st));
+      } else if (pass == 1) {
+        CHECK(gpb_compose_gather_records(d_dense2, &t3, p->d_prefix_desc, S - NCP, S,
+                                         b->page_size, b->row_bytes, d_status, st));
+        CHECK(gpb_compose_consume_fill(d_dense2, &t3, p, S, NCP, d_stag2, (int64_t)stag_rows,
+                                       d_pool2, pool_rows, d_cur, T, b->page_size,
+                                       b->row_bytes, d_status, st));
+      } else {
+        CHECK(gpb_compose_layer_ahead_fill(d_dense2, d_dense2, &t3, p, S, NCP, d_stag2,
+                                           (int64_t)stag_rows, d_pool2, pool_rows, d_cur, T,
+                                           b->page_size, b->row_bytes, d_status, st));
+      }
+      HCHECK(hipStreamSynchronize(st));
+      if (!same_device_bytes(d_stag2, d_stag, stag_rows * RB) ||
+          !same_device_bytes(d_dense2, d_dense, dense_bytes)) {
+        fprintf(stderr, "%s differs from the two-call layer\n",
+                pass == 0 ? "one-launch layer with fill"
+                : pass == 1 ? "consume with fill" : "layer ahead with fill");
+        return 14;
+      }
+      if (pass == 0) {
+        HCHECK(hipMemcpy(d_pool3, d_pool2, pool_bytes, hipMemcpyDeviceToDevice));
+      } else if (!same_device_bytes(d_pool2, d_pool3, pool_bytes)) {
+        fprintf(stderr, "%s leaves another pool\n",
+                pass == 1 ? "consume with fill" : "layer ahead with fill");
+        return 16;
+      }
     }
+    HCHECK(hipFree(d_pool3));
   }
 
   /* fused fill into a copy of the pool */

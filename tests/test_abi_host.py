@@ -270,9 +270,14 @@ def test_layer_groups_argument_checks():
     assert f(groups(good), 1, ctypes.byref(q), 4, 1, 5, 64, None, None) == B.EALIGN
 
 
-def test_layer_fill_argument_checks():
-    f = B.lib.gpb_compose_layer_fill
+@pytest.mark.parametrize("which", ["layer_fill", "consume_fill", "ahead_fill"])
+def test_layer_fill_argument_checks(which):
     a = 0x100000
+    if which == "ahead_fill":
+        def f(*x):
+            return B.lib.gpb_compose_layer_ahead_fill(x[0], a, *x[1:])
+    else:
+        f = getattr(B.lib, "gpb_compose_" + which)
     t = B.Sources([(a, 10), (a, 4)])
     p = B.gpb_plan(*([a] * len(B.PLAN_FIELDS)))
     # dense, table, plan, S, NCP, staging, staging rows, pool, pool rows, cur, T, PS, RB
@@ -288,6 +293,15 @@ def test_layer_fill_argument_checks():
     q.d_pool_locs = None
     assert f(a, ctypes.byref(t.c), ctypes.byref(q), 4, 1, a, 10, a, 100, a, 5, 64, 1152,
              None, None) == B.EINVAL
+    assert f(a, ctypes.byref(t.c), None, 4, 1, a, 10, a, 100, a, 5, 64, 1152,
+             None, None) == B.EINVAL
+    if which == "ahead_fill":
+        # the next layer's dense buffer is required (with prefix pages) and aligned
+        g = B.lib.gpb_compose_layer_ahead_fill
+        assert g(a, None, ctypes.byref(t.c), ctypes.byref(p), 4, 1, a, 10, a, 100, a, 5, 64,
+                 1152, None, None) == B.EINVAL
+        assert g(a, a + 8, ctypes.byref(t.c), ctypes.byref(p), 4, 1, a, 10, a, 100, a, 5, 64,
+                 1152, None, None) == B.EALIGN
 
 
 def test_plan_build_clear_and_writer_counts_checks():

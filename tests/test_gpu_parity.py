@@ -262,13 +262,15 @@ def _check_one_launch(batch, r, layer, want_plan, pool_np, cur_np, orc):
     assert np.array_equal(_host(r.staging_of(layer)), staging), "fused consume staging differs"
 
 
-def _check_layer_ahead(batch, r, layer, want_plan, pool_np, cur_np, orc):
-    """The layer-ahead launch (gpb_compose_layer_ahead) on one batch whose
-    layers share one pool and one set of current rows: after layer l's
-    prefix gather, one launch consumes layer l into its half and gathers
-    layer l + 1's prefix pages into the other half.  Layer l's half and its
-    staging equal the oracle's layer; the other half holds the oracle's
-    prefix pages, and its current slots keep their poison."""
+def _check_layer_ahead(batch, r, layer, want_plan, pool_np, cur_np, orc, fill=False):
+    """The layer-ahead launch (gpb_compose_layer_ahead, or with ``fill``
+    gpb_compose_layer_ahead_fill) on one batch whose layers share one pool
+    and one set of current rows: after layer l's prefix gather, one launch
+    consumes layer l into its half and gathers layer l + 1's prefix pages
+    into the other half.  Layer l's half and its staging equal the oracle's
+    layer; the other half holds the oracle's prefix pages, and its current
+    slots keep their poison.  With the fill, the pool holds each current row
+    at its pool row and no other pool byte changed (restored afterwards)."""
     assert len(r.pools) == 1 and len(r.curs) == 1
     dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
     h = layer % 2
@@ -276,8 +278,16 @@ def _check_layer_ahead(batch, r, layer, want_plan, pool_np, cur_np, orc):
     r.dense[h].fill_(POISON)
     r.dense[1 - h].fill_(POISON)
     r.gather_prefix(layer)
-    r.ahead(layer)
+    (r.ahead_fill if fill else r.ahead)(layer)
     torch.cuda.synchronize()
+    if fill:
+        pool_after = pool_np.reshape(-1, batch.row_bytes).copy()
+        st = np.zeros(batch.staging_rows_total * batch.row_bytes, np.uint8)
+        assert not orc.fill(st, want_plan["staging_rows"], pool_after.reshape(-1),
+                            want_plan["pool_locs"], cur_np, batch.row_bytes)
+        assert np.array_equal(_host(r.pools[0]).reshape(-1, batch.row_bytes), pool_after), \
+            "layer-ahead with fill: pool differs"
+        r.pools[0].copy_(torch.from_numpy(pool_np.reshape(r.pools[0].shape)))
     assert np.array_equal(_host(r.dense_of(layer)), dense), "layer-ahead: consumed half differs"
     assert np.array_equal(_host(r.staging_of(layer)), staging), "layer-ahead: staging differs"
     nxt = _host(r.dense_of(layer + 1))
@@ -309,6 +319,29 @@ def _check_layer_fill(batch, r, layer, want_plan, pool_np, cur_np, orc):
         "layer with fill: staging differs"
     assert np.array_equal(_host(r.pools[k]).reshape(-1, batch.row_bytes), pool_after), \
         "layer with fill: pool differs"
+    r.pools[k].copy_(torch.from_numpy(pool_np.reshape(r.pools[k].shape)))
+
+
+def _check_consume_fill(batch, r, layer, want_plan, pool_np, cur_np, orc):
+    """The prefix records, then the consume with the fused fill
+    (gpb_compose_consume_fill): dense, staging and pool as the oracle's
+    layer and fill; the pool is restored afterwards."""
+    dense, staging = _oracle_layer(batch, want_plan, pool_np, cur_np, orc)
+    pool_after = pool_np.reshape(-1, batch.row_bytes).copy()
+    st = np.zeros(batch.staging_rows_total * batch.row_bytes, np.uint8)
+    assert not orc.fill(st, want_plan["staging_rows"], pool_after.reshape(-1),
+                        want_plan["pool_locs"], cur_np, batch.row_bytes)
+    h, k = layer % 2, layer % len(r.pools)
+    r.staging[h].zero_()
+    r.dense[h].fill_(POISON)
+    r.gather_prefix(layer)
+    r.consume_fill(layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(r.dense_of(layer)), dense), "consume with fill: dense differs"
+    assert np.array_equal(_host(r.staging_of(layer)), staging), \
+        "consume with fill: staging differs"
+    assert np.array_equal(_host(r.pools[k]).reshape(-1, batch.row_bytes), pool_after), \
+        "consume with fill: pool differs"
     r.pools[k].copy_(torch.from_numpy(pool_np.reshape(r.pools[k].shape)))
 
 
@@ -346,20 +379,25 @@ def _random_case(orc, b, layers=2):
     _check_writer_scatters(b, r, layers + 1, want, pool_np, cur_np, orc)
     _check_layer_fill(b, r, layers, want, pool_np, cur_np, orc)
     _check_layer_ahead(b, r, layers + 1, want, pool_np, cur_np, orc)
+    _check_layer_ahead(b, r, layers, want, pool_np, cur_np, orc, fill=True)
+    _check_consume_fill(b, r, layers + 1, want, pool_np, cur_np, orc)
     assert _status(r) == 0
 
 
 @pytest.mark.parametrize("name,consume", [("traced", "fused"), ("opaque", "fused"),
                                           ("traced", "scatter"), ("medium", "fill"),
                                           ("traced", "one_stream"), ("opaque", "one_stream"),
-                                          ("medium", "one_stream")])
+                                          ("medium", "one_stream"), ("traced", "one_stream_fill"),
+                                          ("opaque", "one_stream_fill")])
 def test_layer_ahead_schedule(orc, name, consume):
     """The whole batch with the layer-ahead prefetch.  On two streams (default
     priority): layer l + 1's prefix gather runs on a side stream while layer
     l is consumed on the main stream, ordered only by events.  On one stream
     ("one_stream"): one launch per layer holds layer l's consume and layer
-    l + 1's prefix gather.  Every layer's dense half is poisoned just before
-    its prefix gather is issued; checked layers are copied out right after
+    l + 1's prefix gather ("one_stream_fill": the consume also stores the
+    current rows in the layer's pool, which no prefix page read shares).
+    Every layer's dense half is poisoned just before its prefix gather is
+    issued; checked layers are copied out right after
     their consume (before the half goes to layer l + 2) and compared with the
     oracle: the first four layers, a middle pair and the last pair."""
     b = workloads.make_batch(name)
@@ -385,8 +423,9 @@ def test_layer_ahead_schedule(orc, name, consume):
                 stag[l] = r.staging_of(l).clone()
 
     main = torch.cuda.current_stream()
-    if consume == "one_stream":
-        r.run_layer_ahead(L, main, before_prefetch=poison, after_consume=keep)
+    if consume.startswith("one_stream"):
+        r.run_layer_ahead(L, main, before_prefetch=poison, after_consume=keep,
+                          fill=consume.endswith("fill"))
     else:
         side = torch.cuda.Stream()
         r.run_pipelined(L, main, side, consume=consume, before_prefetch=poison,
