@@ -72,6 +72,8 @@
  *     tensors); h_* pointers are host memory read during the call only.  The
  *     library allocates no device memory and never synchronises: every launch
  *     is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *     (gpb_compose_layer_noalloc works in a static array of the library's
+ *     own, described with it.)
  *     Order between calls is stream order; the caller keeps buffers alive
  *     until the work is done.
  *   - Row payloads are opaque bytes; row_bytes is a multiple of 16 and every
