@@ -158,3 +158,35 @@ def test_noalloc_layer_fills_the_whole_array(orc):
         caller, noalloc, want = _layer_both_ways(gpb, b, orc)
         assert np.array_equal(caller, want)
         assert np.array_equal(noalloc, caller), "tail %d: the layer differs" % tail
+
+
+def test_noalloc_layer_on_random_small_batches(orc):
+    """Random small batches (empty and both-empty requests, page sizes 1 to
+    64, rows of 16 to 64 bytes, several pool entries and writers) one after
+    another through the array: each equals the caller-staging layer and the
+    oracle, whatever the previous batch left in the array."""
+    import gather_plan_build_amd as gpb
+    import pins
+    for i, b in enumerate(pins.random_batches(40, seed=4242)):
+        pool_np, cur_np = pins.tagged_values(b)
+        pools = [torch.from_numpy(pool_np).cuda()]
+        curs = [torch.from_numpy(cur_np).cuda()]
+        r = gpb.ComposeRunner(gpb.BatchMeta.of(b), pools, curs)
+        r.begin_batch()
+        r.dense[0].fill_(POISON)
+        r.layer(0)
+        dense = torch.full_like(r.dense[0], POISON)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        gpb.compose_layer_noalloc(dense, [(pools[0], b.n_pool_pages)] * b.n_pool_entries,
+                                  b.n_writers, b.staging_cap_pages, r.plan, r.S, r.plan.NCP,
+                                  curs[0], r.T, b.page_size, b.row_bytes, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0 and int(r.status.item()) == 0, i
+        want_plan = oracle.plan_for(b, orc)
+        staging = np.zeros(b.staging_rows_total * b.row_bytes, np.uint8)
+        want, bad = oracle.layer_for(b, want_plan, pool_np.reshape(-1), cur_np, staging, orc)
+        assert not bad
+        n = r.S * b.page_size * b.row_bytes
+        assert np.array_equal(r.dense[0].cpu().numpy()[:n], want.reshape(-1)), i
+        assert np.array_equal(dense.cpu().numpy()[:n], want.reshape(-1)), i
+    _say("40 random batches through the array")
