@@ -63,42 +63,60 @@ def _args():
     return ap.parse_args()
 
 
-# the sources the counters depend on: the per-layer kernels and what they
-# include from the library (plan kernels and host entry points elsewhere do
-# not change the gather's traffic)
-DIGEST_FILES = ("gather_plan_build_amd/csrc/compose.hip",
-                "gather_plan_build_amd/csrc/layer_unit.h",
-                "gather_plan_build_amd/csrc/buffer_io.h",
-                "gather_plan_build_amd/csrc/gpb_common.h")
+# The library whose kernels the counters were taken on (GPB_LIB overrides
+# the in-tree build, as it does for the binding).
+LIB = os.environ.get("GPB_LIB", os.path.join(ROOT, "gather_plan_build_amd", "libgpb.so"))
+_BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 
-def _code_of(text):
-    """C/C++ source without comments and with whitespace collapsed, so that
-    a comment edit does not count as a change of the code the counters were
-    taken on."""
-    import re
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return " ".join(text.split())
+def _elf_section(data, name):
+    """Bytes of the named section of a 64-bit little-endian ELF image."""
+    import struct
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    heads = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+             for i in range(shnum)]
+    names = heads[shstrndx][4]
+    for h in heads:
+        at = names + h[0]
+        if data[at:data.index(b"\0", at)].decode() == name:
+            return data[h[4]:h[4] + h[5]]
+    return None
 
 
-def _source_digest():
+def _kernel_digest(lib=None):
+    """Digest of the machine code of the library's gfx950 kernels: the .text
+    of every gfx950 code object in its offload bundles.  It changes when a
+    kernel's code does and not when only host code or comments do, so the
+    counters stay attached to the kernels they were taken on."""
+    import struct
+    with open(lib or LIB, "rb") as f:
+        data = f.read()
+    fatbin = _elf_section(data, ".hip_fatbin") or b""
     h = hashlib.sha256()
-    for name in DIGEST_FILES:
-        with open(os.path.join(ROOT, name)) as f:
-            h.update(name.encode() + _code_of(f.read()).encode())
+    at = fatbin.find(_BUNDLE_MAGIC)
+    while at >= 0:
+        n = struct.unpack_from("<Q", fatbin, at + len(_BUNDLE_MAGIC))[0]
+        q = at + len(_BUNDLE_MAGIC) + 8
+        for _ in range(n):
+            off, size, tlen = struct.unpack_from("<QQQ", fatbin, q)
+            triple = fatbin[q + 24:q + 24 + tlen].decode()
+            q += 24 + tlen
+            if triple.endswith("gfx950"):
+                h.update(_elf_section(fatbin[at + off:at + off + size], ".text") or b"")
+        at = fatbin.find(_BUNDLE_MAGIC, at + len(_BUNDLE_MAGIC))
     return h.hexdigest()[:16]
 
 
 def _traffic(workload):
     """Memory bytes per one-launch-layer launch from the committed rocprofv3
-    counter summary, if it was taken on the current kernel sources."""
+    counter summary, if it was taken on the kernels the library now holds."""
     path = os.path.join(ROOT, "profiles", "compose_layer_%s_counters.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != _source_digest():
+    if rec.get("kernel_digest") != _kernel_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -360,7 +378,8 @@ def _kernel_table(trace_dir, workload, title):
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     lines = ["# rocprofv3 kernel statistics, %s workload (%s)" % (workload, title),
              "# command: " + _profile_commands(trace_dir, workload)["trace"],
-             "# source digest of %s: %s" % (", ".join(DIGEST_FILES), _source_digest()),
+             "# kernel code digest of libgpb.so (.text of its gfx950 code objects): %s"
+             % _kernel_digest(),
              "%-34s %7s %12s %12s %12s %8s" % ("kernel", "calls", "avg_ns", "min_ns",
                                               "max_ns", "pct")]
     for r in stats:
@@ -406,7 +425,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, workload="traced"):
     copy_kib = 1024 * 1024.0
     f_copy, w_copy = max(fetch["copyBuffer"]), max(write["copyBuffer"])
     f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
-    rec = {"workload": workload, "source_digest": _source_digest(),
+    rec = {"workload": workload, "kernel_digest": _kernel_digest(),
            "commands": _profile_commands(trace_dir, workload),
            "calibration": {"copy_bytes": int(copy_kib * 1024), "fetch_kib": f_copy,
                            "write_kib": w_copy, "fetch_scale": f_scale,
