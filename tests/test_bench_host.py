@@ -35,3 +35,22 @@ def test_profile_commands_name_the_workload_and_output_dir():
     assert c["summary"].endswith("--workload opaque")
     t = bench._profile_commands(os.path.join(ROOT, "out", "prof_trace"))
     assert "--workload" not in t["trace"]
+
+
+def test_kernel_digest_reads_the_library_code_objects(tmp_path):
+    """The counters' key: the digest of the gfx950 kernel code in libgpb.so
+    (found through its offload bundles) is a stable 16-hex-digit value, the
+    same for a byte copy of the library, and a library without kernels gives
+    the digest of nothing."""
+    import hashlib
+    import shutil
+    d = bench._kernel_digest()
+    assert len(d) == 16 and int(d, 16) >= 0
+    assert d != hashlib.sha256(b"").hexdigest()[:16]
+    copy = tmp_path / "libcopy.so"
+    shutil.copyfile(bench.LIB, copy)
+    assert bench._kernel_digest(str(copy)) == d
+    with open(bench.LIB, "rb") as f:
+        data = f.read()
+    assert bench._elf_section(data, ".hip_fatbin") is not None
+    assert bench._elf_section(data, ".no_such_section") is None
