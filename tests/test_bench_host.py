@@ -39,9 +39,8 @@ def test_profile_commands_name_the_workload_and_output_dir():
 
 def test_kernel_digest_reads_the_library_code_objects(tmp_path):
     """The counters' key: the digest of the gfx950 kernel code in libgpb.so
-    (found through its offload bundles) is a stable 16-hex-digit value, the
-    same for a byte copy of the library, and a library without kernels gives
-    the digest of nothing."""
+    (found through its offload bundles) is a stable 16-hex-digit value, not
+    the digest of nothing, and the same for a byte copy of the library."""
     import hashlib
     import shutil
     d = bench._kernel_digest()
