@@ -570,6 +570,34 @@ def test_random_small_batches(orc, seed):
     _say("seed", seed, "done")
 
 
+def test_random_larger_geometries(orc):
+    """300 seeded random batches of larger geometries through every layer
+    path: up to 40 requests, many of them empty on one side, pages of 1 to
+    64 rows, rows of 16 to 4,096 bytes, up to 8 pool entries and 8 writers,
+    spare staging pages."""
+    rng = np.random.default_rng(2026)
+    done = 0
+    while done < 300:
+        ps = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64]))
+        rb = int(rng.choice([16, 32, 48, 144, 320, 336, 656, 1024, 1152, 2064, 4096]))
+        bs = int(rng.integers(0, 41))
+        P = rng.integers(0, 12, bs).astype(np.int32)
+        P[rng.random(bs) < 0.3] = 0
+        c = rng.integers(0, 5 * ps + 1, bs).astype(np.int32)
+        c[rng.random(bs) < 0.3] = 0
+        need = int(P.sum() + ((c + ps - 1) // ps).sum())
+        n_pool = need + 1 + int(rng.integers(0, 200))
+        if n_pool * ps * rb > (64 << 20):
+            continue
+        pages = rng.choice(np.arange(1, n_pool), need, replace=False).astype(np.int32)
+        np_, w = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        cap = workloads.staging_cap_for(int(c.sum()), bs, ps) + int(rng.integers(0, 4))
+        _random_case(orc, workloads.Batch("larger", bs, ps, rb, n_pool, np_, w, cap, P, c,
+                                          pages))
+        done += 1
+    _say("300 larger random batches byte-exact")
+
+
 def test_many_requests_past_the_lds_stage(orc):
     """bs = 1500 exceeds the requests staged in LDS (1024): the plan kernels
     search the bases in global memory."""
