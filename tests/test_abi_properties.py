@@ -53,7 +53,10 @@ def batches(draw):
     return bs, ps, rb, npp, np_, w, cap, P, c, pages
 
 
-@settings(max_examples=600, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+# derandomized: every run draws the same 600 batches (a one-off run of 20,000
+# random draws agreed as well)
+@settings(max_examples=600, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow])
 @given(batches())
 def test_host_validation_agrees_with_the_oracle(b):
     bs, ps, rb, npp, np_, w, cap, P, c, pages = b
