@@ -51,6 +51,10 @@ def _args():
     ap.add_argument("--summarize-extras", metavar="TRACE",
                     help="write profiles/compose_<workload>_extras_kernels.txt from the "
                          "rocprofv3 kernel-trace directory of a default run and exit")
+    ap.add_argument("--summarize-extras-counters", nargs=2, metavar=("FETCH", "WRITE"),
+                    help="write profiles/compose_<workload>_extras_counters.txt from the "
+                         "FETCH_SIZE and WRITE_SIZE runs of a default run with the extras "
+                         "and exit")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the headline path only (no prefetch split, fused fill "
                          "or twin): the mode the profiler runs use")
@@ -374,6 +378,63 @@ def summarize_extras(trace_dir, workload="traced"):
     print("\n".join(lines))
 
 
+EXTRAS_COUNTER_COMMAND = (
+    "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {counter} --output-format csv "
+    "-d $OUT/prof_extras_{what} -o {what} -- python3 $REPO/bench.py "
+    "--steps 1 --warmup 0 --cpu-seconds 0 --calibration-copy-mib 1024")
+
+
+def summarize_extras_counters(fetch_dir, write_dir, workload="traced"):
+    """profiles/compose_<workload>_extras_counters.txt: bytes per dispatch
+    below L2 of every library kernel in a default run with the extras, per
+    kernel and grid size (one launch shape per line: the one-launch layer,
+    the consume alone, the record halves, ...), from FETCH_SIZE and
+    WRITE_SIZE, each scaled by what it reads for a 1 GiB copy in the same
+    run."""
+    import re
+
+    def per_shape(directory, counter):
+        acc = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            m = re.search(r"(k_\w+(<[^>]*>)?|copyBuffer)", r["Kernel_Name"])
+            name = m.group(0).replace(" ", "") if m else r["Kernel_Name"][:40]
+            acc.setdefault((name, int(r.get("Grid_Size") or 0)), []).append(
+                float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = per_shape(fetch_dir, "FETCH_SIZE"), per_shape(write_dir, "WRITE_SIZE")
+    copy_kib = 1024 * 1024.0
+    f_scale = copy_kib / max(v for (k, g), vs in fetch.items() if k == "copyBuffer" for v in vs)
+    w_scale = copy_kib / max(v for (k, g), vs in write.items() if k == "copyBuffer" for v in vs)
+    out = os.path.relpath(os.path.dirname(os.path.abspath(fetch_dir)), ROOT)
+    flag = "" if workload == "traced" else " --workload " + workload
+    lines = ["# rocprofv3 counters below L2 per dispatch, %s workload, default run with "
+             "the extras; FETCH_SIZE scaled by %.4f and WRITE_SIZE by %.4f (what each reads "
+             "for a 1 GiB copy in the same run)" % (workload, f_scale, w_scale)]
+    for what, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        cmd = EXTRAS_COUNTER_COMMAND.format(counter=counter, what=what)
+        lines.append("# command: " + cmd.replace("$OUT", "$REPO/" + out)
+                     .replace("bench.py", "bench.py" + flag, 1))
+    lines.append("# kernel code digest of libgpb.so: %s" % _kernel_digest())
+    lines.append("%-34s %10s %6s %14s %14s" % ("kernel", "workgroups", "calls", "read_MB",
+                                               "write_MB"))
+    for key in sorted(set(fetch) & set(write)):
+        name, grid = key
+        if not name.startswith("k_"):
+            continue
+        fk = sum(fetch[key]) / len(fetch[key])
+        wk = sum(write[key]) / len(write[key])
+        lines.append("%-34s %10d %6d %14.1f %14.1f" % (
+            name, grid // 64 if "plan" not in name and "fill_zero" not in name else grid // 256,
+            len(fetch[key]), fk * f_scale * 1024 / 1e6, wk * w_scale * 1024 / 1e6))
+    path = os.path.join(ROOT, "profiles", "compose_%s_extras_counters.txt" % workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def _kernel_table(trace_dir, workload, title):
     stats = _csv_rows(trace_dir, "kernel_stats.csv")
     lines = ["# rocprofv3 kernel statistics, %s workload (%s)" % (workload, title),
@@ -503,6 +564,9 @@ def main():
         return
     if a.summarize_trace:
         summarize_trace(a.summarize_trace, workload=a.workload)
+        return
+    if a.summarize_extras_counters:
+        summarize_extras_counters(*a.summarize_extras_counters, workload=a.workload)
         return
     if a.summarize_extras:
         summarize_extras(a.summarize_extras, workload=a.workload)
